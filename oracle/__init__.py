@@ -1,0 +1,94 @@
+"""ctypes wrapper of the plain-C fp64 oracle (sv_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the HIP
+library and never calls it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sv_oracle.c")
+_LIB = os.path.join(_HERE, "libsv_oracle.so")
+
+STATUS_BAD_TOKEN, STATUS_NAN, STATUS_POSINF, STATUS_EMPTY_ROW, STATUS_BAD_UNIFORM = 1, 2, 4, 8, 16
+TOPK = 32
+
+
+def build() -> str:
+    """Compile the oracle with gcc (plain C99, no fast-math, no FMA contraction)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                           "-shared", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.orc_verify.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                   P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.orc_verify.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class OracleResult(dict):
+    __getattr__ = dict.__getitem__
+
+
+def verify(target, draft, draft_tokens, uniforms, temperature, dtype, aux=True) -> OracleResult:
+    """Run the oracle.  target [B,k+1,V] and draft [B,k,V] are float32 arrays, or
+    uint16 bf16 bit patterns with dtype=1; draft_tokens [B,k] int32; uniforms
+    [B,k+2] float32.  Returns a dict of numpy arrays."""
+    lib = _load()
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    k = K1 - 1
+    greedy = float(temperature) == 0.0
+    want = np.float32 if dtype == 0 else np.uint16
+    assert target.dtype == want
+    draft = None if (greedy and draft is None) else np.ascontiguousarray(draft, dtype=want)
+    if draft is not None:
+        assert draft.shape == (B, k, V)
+    tokens = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, k)
+    u = None if (greedy and uniforms is None) else np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, K1 + 1)
+    r = OracleResult(
+        accepted_len=np.empty(B, np.int32), out_tokens=np.empty((B, K1), np.int32),
+        topk_val=np.empty((B, K1, TOPK), np.float32), topk_idx=np.empty((B, K1, TOPK), np.int32),
+        status=np.empty(B, np.int32))
+    if aux:
+        r.update(lse_target=np.full((B, K1), np.nan), lse_draft=np.full((B, k), np.nan),
+                 p_tok=np.full((B, k), np.nan), q_tok=np.full((B, k), np.nan),
+                 margin_accept=np.full((B, k), np.nan), margin_cdf=np.full(B, np.nan))
+    g = r.get
+    rc = lib.orc_verify(B, k, V, int(dtype), float(temperature), _ptr(target), _ptr(draft), _ptr(tokens), _ptr(u),
+                        _ptr(r["accepted_len"]), _ptr(r["out_tokens"]), _ptr(r["topk_val"]), _ptr(r["topk_idx"]),
+                        _ptr(r["status"]), _ptr(g("lse_target")), _ptr(g("lse_draft")), _ptr(g("p_tok")),
+                        _ptr(g("q_tok")), _ptr(g("margin_accept")), _ptr(g("margin_cdf")))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return r
+
+
+def verify_workload(w, aux=True) -> OracleResult:
+    """Oracle on an sv_inputs.Workload."""
+    return verify(w.target, None if w.temperature == 0 else w.draft, w.draft_tokens,
+                  None if w.temperature == 0 else w.uniforms, w.temperature, w.dtype, aux=aux)
