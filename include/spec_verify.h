@@ -1,0 +1,139 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-sampling verification library for
+ * AMD MI355X (gfx950).
+ *
+ * The operation (ReSpec notes, "2 . background": one-shot acceptance test Eq.1
+ * of Leviathan et al. 2023 and the residual r(x) = max(0, p - q) / sum max(0, p - q);
+ * ReSpec blog, speculative-decoding steps 1-4; slime/Notion post, introduction):
+ * for each of B sequences with k drafted tokens x_0..x_{k-1},
+ *   p_i = softmax(target_logits[b,i,:] / T)  for i = 0..k,
+ *   q_i = softmax(draft_logits[b,i,:] / T)   for i = 0..k-1,
+ *   draft token i is accepted while u[b,i] < min(1, p_i(x_i) / q_i(x_i));
+ *   at the first rejection j the token is redrawn from the residual
+ *   max(0, p_j - q_j), normalised, by inverse CDF with u[b,k];
+ *   if all k drafts pass, a bonus token is drawn from p_k with u[b,k+1].
+ * With T == 0 the step is greedy: draft i is accepted while it equals the
+ * argmax of target row i (lowest index on ties), and the argmax of the first
+ * mismatching row (or of row k) is emitted.
+ * In both modes the 32 largest target logits of every verified position are
+ * returned, the soft targets stored for drafter distillation (ReSpec notes,
+ * "4 . G2", worked example: V = 151936, top-K = 32).
+ *
+ * Conventions where the pages are silent:
+ *   - inverse CDF walks tokens in ascending index and takes the first x whose
+ *     cumulative mass exceeds u * R (R the unnormalised total); tokens of zero
+ *     mass are never drawn;
+ *   - q_i(x_i) == 0 counts as ratio +inf when p_i(x_i) > 0, else 0;
+ *   - a residual with no mass left (only through rounding) falls back to p_j;
+ *   - top-32 order is (value descending, index ascending) under float
+ *     comparison (-0.0 == +0.0); values are the raw target logits as fp32; rows
+ *     with V < 32 pad with (-inf, -1); rows holding a NaN give (NaN, -1).
+ *
+ * Results are deterministic: vocabulary tiles have a fixed size and every
+ * reduction runs in a fixed order, so a row's result does not depend on B, on
+ * the other rows or on the launch size.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_TOPK 32
+
+/* element type of the logits */
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
+
+/* return codes (host-detected; nothing is launched when one is returned) */
+#define SV_OK 0
+#define SV_ERR_NULL (-1)        /* a required pointer is NULL */
+#define SV_ERR_SHAPE (-2)       /* B < 0, k < 0, V < 1, a row stride < V, or sizes too large */
+#define SV_ERR_TEMPERATURE (-3) /* temperature < 0, NaN or infinite */
+#define SV_ERR_DTYPE (-4)       /* dtype not SV_F32 / SV_BF16 */
+#define SV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than spec_verify_workspace_bytes */
+#define SV_ERR_HIP (-6)         /* a HIP runtime call or the kernel launch failed */
+#define SV_ERR_DEVICE (-7)      /* current device is not usable (no cooperative launch) */
+
+/* per-sequence data-error bits written to aux->status (device side) */
+#define SV_STATUS_BAD_TOKEN 1    /* a draft token is outside [0, V) */
+#define SV_STATUS_NAN 2          /* a used row holds a NaN */
+#define SV_STATUS_POSINF 4       /* sampling: a used row holds +inf (softmax undefined) */
+#define SV_STATUS_EMPTY_ROW 8    /* sampling: a used row is all -inf (no distribution) */
+#define SV_STATUS_BAD_UNIFORM 16 /* sampling: a uniform is outside [0, 1) */
+#define SV_STATUS_SYNC_TIMEOUT 32 /* internal: a cross-workgroup wait gave up (never expected) */
+
+typedef struct {
+    int32_t B;                  /* sequences, >= 0 (0: nothing to do) */
+    int32_t k;                  /* drafted tokens per sequence, >= 0 */
+    int32_t V;                  /* vocabulary size, >= 1 */
+    int32_t dtype;              /* sv_dtype_t of both logits tensors */
+    int64_t target_row_stride;  /* elements between target rows (b,i) and (b,i+1), and
+                                   between (b,k) and (b+1,0); 0 means V */
+    int64_t draft_row_stride;   /* same for draft rows; 0 means V */
+    float temperature;          /* > 0: sampling; == 0: greedy */
+} sv_shape_t;
+
+/* optional outputs (device pointers; any may be NULL) */
+typedef struct {
+    int32_t *status;     /* [B]    SV_STATUS_* bits; 0 = valid sequence */
+    float *lse_target;   /* [B,k+1] ln sum_x exp(t_x / T)   (sampling only) */
+    float *lse_draft;    /* [B,k]   ln sum_x exp(d_x / T)   (sampling only) */
+    float *p_tok;        /* [B,k]   p_i(x_i)                (sampling only) */
+    float *q_tok;        /* [B,k]   q_i(x_i)                (sampling only) */
+} sv_aux_t;
+
+/* Bytes of device workspace one call with this shape needs. */
+size_t spec_verify_workspace_bytes(const sv_shape_t *shape);
+
+/*
+ * Enqueue one verification step on `stream` (a hipStream_t; NULL = default
+ * stream) and return without synchronising.  Outputs are valid once the
+ * stream has reached this point.
+ *
+ * Inputs (device pointers, caller-owned, row-major, 16-byte aligned rows run
+ * fastest; other alignments are accepted):
+ *   target_logits [B, k+1, V] with row stride target_row_stride
+ *   draft_logits  [B, k, V]   with row stride draft_row_stride; ignored and
+ *                             may be NULL when temperature == 0
+ *   draft_tokens  [B, k] int32
+ *   uniforms      [B, k+2] fp32 in [0,1): u[0..k-1] acceptance, u[k] residual
+ *                 draw, u[k+1] bonus draw; ignored and may be NULL when
+ *                 temperature == 0
+ * Outputs (device pointers, caller-owned):
+ *   accepted_len  [B] int32, in [0, k]; -1 for a sequence with a data error
+ *   out_tokens    [B, k+1] int32: drafts 0..j-1, the drawn token at j, -1 after;
+ *                 all -1 for a sequence with a data error
+ *   topk_val      [B, k+1, 32] fp32 and topk_idx [B, k+1, 32] int32
+ *   aux           optional outputs; NULL for none
+ * Workspace: device memory of at least spec_verify_workspace_bytes(shape)
+ *   bytes, 256-byte aligned, zero-filled before its first use.  Every call
+ *   leaves it zero-filled again for the next one.  Calls that share a
+ *   workspace must not overlap in time.
+ * Errors: host-detectable argument errors return a negative SV_ERR_* code
+ *   before anything is enqueued.  Data errors (bad token, NaN, +inf, all -inf
+ *   row, bad uniform) cannot be seen without a device sync; they set the
+ *   SV_STATUS_* bits of that sequence and make its accepted_len and
+ *   out_tokens -1.
+ * The library allocates no memory and keeps no per-call state; it is safe to
+ * call from several host threads with separate workspaces.
+ */
+int spec_verify(const sv_shape_t *shape,
+                const void *target_logits, const void *draft_logits,
+                const int32_t *draft_tokens, const float *uniforms,
+                int32_t *accepted_len, int32_t *out_tokens,
+                float *topk_val, int32_t *topk_idx,
+                const sv_aux_t *aux,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a return code. */
+const char *spec_verify_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,85 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function the header declares, sizes its workspace, describes its error codes
+and rejects bad arguments on the host before anything is enqueued."""
+import ctypes
+
+import pytest
+
+import draft_verification_spec_amd as sv
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = sv.declared_functions()
+    assert set(names) == {"spec_verify", "spec_verify_workspace_bytes", "spec_verify_error_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_error_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        s = sv.spec_verify_error_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in sv.spec_verify_error_string(-99)
+
+
+def test_workspace_bytes():
+    f = sv.spec_verify_workspace_bytes
+    small = f(sv.make_shape(2, 3, 1000, sv.SV_F32, 1.0))
+    big = f(sv.make_shape(32, 3, 151936, sv.SV_BF16, 1.0))
+    assert 0 < small < big
+    assert big < 64 << 20                      # a few MB at the steady-state shape
+    assert f(sv.make_shape(-1, 3, 10, 0, 1.0)) == 0
+    assert f(sv.make_shape(1, 3, 0, 0, 1.0)) == 0
+    assert f(sv.make_shape(1, 3, (1 << 20) + 1, 0, 1.0)) == 0
+    assert f(sv.make_shape(0, 3, 100, 0, 1.0)) > 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _call(shape, **over):
+    a = dict(t=FAKE, d=FAKE, x=FAKE, u=FAKE, acc=FAKE, out=FAKE, tv=FAKE, ti=FAKE, ws=FAKE * 16,
+             wsb=1 << 30)
+    a.update(over)
+    return sv.spec_verify(shape, a["t"], a["d"], a["x"], a["u"], a["acc"], a["out"], a["tv"], a["ti"], None,
+                          a["ws"], a["wsb"], None)
+
+
+def test_host_validation_codes():
+    good = sv.make_shape(2, 3, 1000, sv.SV_F32, 1.0)
+    assert sv.spec_verify(None, 0, 0, 0, 0, 0, 0, 0, 0, None, 0, 0, None) == sv.SV_ERR_NULL
+    assert _call(sv.make_shape(2, 3, 1000, 7, 1.0)) == sv.SV_ERR_DTYPE
+    assert _call(sv.make_shape(-1, 3, 1000, 0, 1.0)) == sv.SV_ERR_SHAPE
+    assert _call(sv.make_shape(2, -1, 1000, 0, 1.0)) == sv.SV_ERR_SHAPE
+    assert _call(sv.make_shape(2, 3, 0, 0, 1.0)) == sv.SV_ERR_SHAPE
+    assert _call(sv.make_shape(2, 3, 1000, 0, 1.0, target_row_stride=999)) == sv.SV_ERR_SHAPE
+    assert _call(sv.make_shape(2, 3, 1000, 0, 1.0, draft_row_stride=10)) == sv.SV_ERR_SHAPE
+    assert _call(sv.make_shape(2, 3, 1000, 0, -1.0)) == sv.SV_ERR_TEMPERATURE
+    assert _call(sv.make_shape(2, 3, 1000, 0, float("nan"))) == sv.SV_ERR_TEMPERATURE
+    assert _call(sv.make_shape(2, 3, 1000, 0, float("inf"))) == sv.SV_ERR_TEMPERATURE
+    assert _call(good, t=None) == sv.SV_ERR_NULL
+    assert _call(good, d=None) == sv.SV_ERR_NULL          # sampling needs draft logits
+    assert _call(good, u=None) == sv.SV_ERR_NULL          # and uniforms
+    assert _call(good, x=None) == sv.SV_ERR_NULL
+    assert _call(good, tv=None) == sv.SV_ERR_NULL
+    assert _call(good, ws=None) == sv.SV_ERR_WORKSPACE
+    need = sv.spec_verify_workspace_bytes(good)
+    assert _call(good, wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    assert _call(good, ws=FAKE * 16 + 8) == sv.SV_ERR_WORKSPACE   # 256-byte alignment
+    # B == 0 is a valid empty call: nothing to enqueue
+    assert _call(sv.make_shape(0, 3, 1000, 0, 1.0)) == sv.SV_OK
+
+
+def test_product_path_never_touches_the_oracle():
+    """Neither the binding nor the HIP source names the oracle package."""
+    import glob
+    import os
+    pkg = os.path.dirname(sv.__file__)
+    for f in glob.glob(os.path.join(pkg, "*.py")) + glob.glob(os.path.join(pkg, "csrc", "*")):
+        text = open(f).read()
+        assert "import oracle" not in text and "sv_oracle" not in text and "orc_verify" not in text, f

@@ -1,0 +1,328 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: accepted_len, out_tokens and top-32 indices identical except decisions the
+oracle flags within 1e-5 of their boundary (under 0.1% of positions); top-32
+values bit-exact; p_tok/q_tok/lse within 1e-5 relative for fp32 inputs and 2e-3
+for bf16 inputs; greedy bit-exact.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import sv_inputs
+import golden_cases
+from compare import FLAG, compare_decisions, compare_topk, gpu_to_numpy, rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def log(msg):
+    print(f"[gpu-test] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import draft_verification_spec_amd as m
+    m.load_library()      # raises when the HIP library was not built
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc(oracle_mod):
+    return oracle_mod
+
+
+def run_gpu(sv, w, aux=True):
+    log(f"spec_verify {w.name} B={w.B} k={w.k} V={w.V} dtype={sv_inputs.DTYPE_NAME[w.dtype]} T={w.temperature}")
+    t, d, x, u = sv.to_device(w)
+    greedy = w.temperature == 0
+    r = sv.verify(t, None if greedy else d, x, None if greedy else u, w.temperature, aux=aux)
+    torch.cuda.synchronize()
+    return gpu_to_numpy(r)
+
+
+def check_parity(orc_res, gpu, w, exceptions_budget=True):
+    k = w.k
+    rep = compare_decisions(orc_res, gpu, k)
+    assert not rep["fails"], rep["fails"][:5]
+    if exceptions_budget:
+        assert rep["exc_pos"] <= 0.001 * rep["positions"], rep
+    bad_idx, vals_ok = compare_topk(orc_res, gpu)
+    assert len(bad_idx) == 0, bad_idx[:5]
+    assert vals_ok
+    if w.temperature > 0 and gpu.get("p_tok") is not None:
+        tol = 1e-5 if w.dtype == sv_inputs.F32 else 2e-3
+        ok = orc_res["status"] == 0
+        for key in ("p_tok", "q_tok", "lse_target", "lse_draft"):
+            e = rel_err(orc_res[key][ok], gpu[key][ok])
+            assert e < tol, (key, e)
+    return rep
+
+
+# ------------------------------------------------------------------ hand cases
+CASES = golden_cases.load()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_hand_exact_on_gpu(sv, case):
+    w = golden_cases.workload(case)
+    g = run_gpu(sv, w)
+    golden_cases.check(case, g, sampling_aux=False)
+    e = case["expect"]
+    for key in ("p_tok", "q_tok"):
+        if key in e:
+            np.testing.assert_allclose(g[key][0][: len(e[key])], e[key], rtol=1e-6, atol=0)
+
+
+# ------------------------------------------------------------------ workloads
+def test_tiny_config(sv, orc):
+    w = sv_inputs.tiny()
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
+
+
+@pytest.mark.parametrize("seed", [1101, 1102])
+def test_tiny_many_sequences(sv, orc, seed):
+    w = sv_inputs.tiny(seed=seed, B=256)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
+
+
+def test_exception_budget_many_positions(sv, orc):
+    """4096 positions at the steady-state value distribution (V cut to 12,345,
+    a ragged 4-tile row): mismatches must all be flagged and under 0.1%."""
+    w = sv_inputs.steady(seed=1201, B=1024, V=12345)
+    rep = check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
+    log(f"exceptions {rep['exc_pos']} of {rep['positions']} positions")
+
+
+def test_steady_small_batch_full_vocab(sv, orc):
+    w = sv_inputs.steady(B=4)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
+
+
+def test_steady_full_size_sampled(sv, orc):
+    """Full B=32 batch in one launch; the oracle recomputes 8 sequences."""
+    w = sv_inputs.steady()
+    g = run_gpu(sv, w)
+    bs = np.array([0, 5, 11, 16, 21, 26, 30, 31])
+    ws = w.subset(bs)
+    o = orc.verify_workload(ws)
+    gs = {k: (v[bs] if v is not None else None) for k, v in g.items()}
+    check_parity(o, gs, ws, exceptions_budget=False)
+    assert (g["status"] == 0).all()
+    assert ((g["accepted_len"] >= 0) & (g["accepted_len"] <= 3)).all()
+
+
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_longtail(sv, orc, B):
+    w = sv_inputs.longtail(B)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+
+
+def test_grpo_full_size_sampled(sv, orc):
+    w = sv_inputs.grpo()
+    g = run_gpu(sv, w)
+    bs = np.array([0, 1, 7, 8, 100, 200, 254, 255])
+    ws = w.subset(bs)
+    o = orc.verify_workload(ws)
+    gs = {k: (v[bs] if v is not None else None) for k, v in g.items()}
+    check_parity(o, gs, ws, exceptions_budget=False)
+    # rollouts of one prompt share target row 0: identical top-32 there
+    assert np.array_equal(g["topk_idx"][0, 0], g["topk_idx"][7, 0])
+
+
+def test_wide_sampling_sampled(sv, orc):
+    w = sv_inputs.wide()
+    g = run_gpu(sv, w)
+    bs = np.array([0, 13, 31])
+    ws = w.subset(bs)
+    o = orc.verify_workload(ws)
+    gs = {k: (v[bs] if v is not None else None) for k, v in g.items()}
+    check_parity(o, gs, ws, exceptions_budget=False)
+
+
+def test_wide_greedy_bit_exact(sv, orc):
+    w = sv_inputs.wide(greedy=True)
+    g = run_gpu(sv, w)
+    o = orc.verify_workload(w)
+    np.testing.assert_array_equal(o["accepted_len"], g["accepted_len"])
+    np.testing.assert_array_equal(o["out_tokens"], g["out_tokens"])
+    np.testing.assert_array_equal(o["status"], g["status"])
+    np.testing.assert_array_equal(o["topk_idx"], g["topk_idx"])
+    np.testing.assert_array_equal(o["topk_val"].view(np.uint32), g["topk_val"].view(np.uint32))
+
+
+def test_greedy_bf16_prefix_matches(sv, orc):
+    """Greedy on bf16 with drafts equal to the target argmax for a prefix of random length."""
+    w = sv_inputs.steady(seed=1301, B=16, V=50000)
+    w.temperature = 0.0
+    rng = np.random.default_rng(5)
+    t = w.target_f32()
+    am = t.argmax(axis=2)
+    for b in range(w.B):
+        n = rng.integers(0, w.k + 1)
+        w.draft_tokens[b, :n] = am[b, :n]
+    o = orc.verify_workload(w)
+    g = run_gpu(sv, w)
+    for key in ("accepted_len", "out_tokens", "status", "topk_idx"):
+        np.testing.assert_array_equal(o[key], g[key], err_msg=key)
+    assert len(set(o["accepted_len"].tolist())) > 1
+
+
+# ------------------------------------------------------------------ edges
+@pytest.mark.parametrize("V", [1, 7, 31, 32, 33, 4096, 4097, 3 * 4096 + 17])
+@pytest.mark.parametrize("dtype", [sv_inputs.F32, sv_inputs.BF16])
+def test_vocab_edges(sv, orc, V, dtype):
+    w = sv_inputs.make_workload("edge", 6, 2, V, dtype, 1.0, 1400 + V, 2.0, 0.7)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+    wg = sv_inputs.make_workload("edge_greedy", 6, 2, V, dtype, 0.0, 1400 + V, 2.0, 0.7, draft_T=0.0)
+    o, g = orc.verify_workload(wg), run_gpu(sv, wg)
+    for key in ("accepted_len", "out_tokens", "topk_idx"):
+        np.testing.assert_array_equal(o[key], g[key], err_msg=key)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_k_zero(sv, orc, T):
+    w = sv_inputs.make_workload("k0", 5, 0, 9000, sv_inputs.BF16, T, 1501, 2.0, 0.5)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+
+
+def test_largest_vocab(sv, orc):
+    V = 1 << 20
+    w = sv_inputs.make_workload("maxV", 1, 1, V, sv_inputs.BF16, 1.0, 1601, 3.0, 1.0)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+
+
+def test_temperatures(sv, orc):
+    for T in (0.25, 0.7, 2.0):
+        w = sv_inputs.make_workload("temp", 8, 3, 20000, sv_inputs.F32, T, 1701, 3.0, 1.0)
+        check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+
+
+def test_top32_ties_and_constant_rows(sv, orc):
+    """Heavy bf16 ties at the cut, a constant row (every element tied: exact
+    fallback path), a row of -inf but 3 tokens, and -0.0/+0.0 ties."""
+    V = 151936
+    w = sv_inputs.make_workload("ties", 2, 2, V, sv_inputs.BF16, 0.0, 1801, 1.0, 1.0, draft_T=0.0)
+    rng = np.random.default_rng(3)
+    x = np.round(rng.standard_normal((2, 3, V)) * 2).astype(np.float32)
+    x[0, 1] = 0.0
+    x[0, 2] = -np.inf
+    x[0, 2, [5, 70000, 151935]] = [1.0, 1.0, -1.0]
+    x[1, 0, rng.integers(0, V, 100)] = -0.0
+    w.target = sv_inputs.bf16_round(x)
+    w.draft_tokens[:] = 0
+    o, g = orc.verify_workload(w), run_gpu(sv, w)
+    for key in ("accepted_len", "out_tokens", "topk_idx", "status"):
+        np.testing.assert_array_equal(o[key], g[key], err_msg=key)
+    np.testing.assert_array_equal(o["topk_val"].view(np.uint32), g["topk_val"].view(np.uint32))
+
+
+def test_data_errors(sv, orc):
+    V = 5000
+    w = sv_inputs.make_workload("errors", 8, 2, V, sv_inputs.F32, 1.0, 1901, 2.0, 0.5)
+    w.draft_tokens[1, 1] = V             # bad token
+    w.draft[2, 0, 17] = np.nan           # NaN in a draft row
+    w.target[3, 2, 4000] = np.inf        # +inf in the bonus row
+    w.draft[4, 1, :] = -np.inf           # empty draft row
+    w.uniforms[5, 3] = 1.0               # bad uniform
+    w.target[6, 0, 9] = np.nan           # NaN in a target row (top-32 slot NaN)
+    w.target[6, 0, 10] = np.inf
+    o, g = orc.verify_workload(w), run_gpu(sv, w)
+    for key in ("status", "accepted_len", "out_tokens", "topk_idx"):
+        np.testing.assert_array_equal(o[key], g[key], err_msg=key)
+    assert g["status"].tolist() == [0, 1, 2, 4, 8, 16, 2, 0]
+
+
+# ------------------------------------------------------------------ layout
+def test_strided_and_unaligned_rows(sv, orc):
+    w = sv_inputs.make_workload("stride", 3, 2, 10001, sv_inputs.BF16, 1.0, 2001, 2.0, 0.6)
+    base = run_gpu(sv, w)
+    t, d, x, u = sv.to_device(w)
+    pad = 64
+    tb = torch.zeros(3, 3, 10001 + pad, dtype=t.dtype, device=t.device)
+    db = torch.zeros(3, 2, 10001 + pad, dtype=t.dtype, device=t.device)
+    tb[..., :10001] = t
+    db[..., :10001] = d
+    r = sv.verify(tb[..., :10001], db[..., :10001], x, u, 1.0, aux=True)
+    g = gpu_to_numpy(r)
+    for key in ("accepted_len", "out_tokens", "topk_idx", "topk_val", "p_tok", "lse_target"):
+        np.testing.assert_array_equal(base[key], g[key], err_msg=key)
+    # V=10001 bf16 rows start at odd 16-byte phases: the element-wise load path
+    check_parity(orc.verify_workload(w), base, w, exceptions_budget=False)
+
+
+# ------------------------------------------------------------------ determinism
+def test_deterministic_and_launch_size_invariant(sv):
+    w = sv_inputs.steady(seed=2101, B=3)
+    a = run_gpu(sv, w)
+    b = run_gpu(sv, w)
+    os.environ["SV_GRID_LIMIT"] = "40"
+    try:
+        c = run_gpu(sv, w)
+    finally:
+        del os.environ["SV_GRID_LIMIT"]
+    for key in a:
+        if a[key] is not None:
+            np.testing.assert_array_equal(a[key].view(np.uint8), b[key].view(np.uint8), err_msg=key)
+            np.testing.assert_array_equal(a[key].view(np.uint8), c[key].view(np.uint8), err_msg=key)
+
+
+def test_batch_invariance(sv):
+    w = sv_inputs.longtail(4)
+    full = run_gpu(sv, w)
+    for b in range(4):
+        one = run_gpu(sv, w.subset([b]))
+        for key in full:
+            if full[key] is not None:
+                np.testing.assert_array_equal(full[key][b:b + 1].view(np.uint8), one[key].view(np.uint8),
+                                              err_msg=key)
+
+
+def test_workspace_left_zero_for_any_next_shape(sv, orc):
+    """Regression: one workspace serves calls of growing and shrinking shapes;
+    each call must leave every byte zero, or the next layout would read stale
+    records as counters."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for w in (sv_inputs.steady(seed=2201, B=2, V=20000), sv_inputs.steady(seed=2204, B=12, V=20000),
+              sv_inputs.tiny(seed=2202, B=9), sv_inputs.steady(seed=2203, B=1)):
+        t, d, x, u = sv.to_device(w)
+        r = sv.verify(t, d, x, u, w.temperature, aux=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0
+        check_parity(orc.verify_workload(w), gpu_to_numpy(r), w, exceptions_budget=False)
+    wg = sv_inputs.wide(seed=2205, B=3, k=4, V=30000, greedy=True)
+    t, _, x, _ = sv.to_device(wg)
+    sv.verify(t, None, x, None, 0.0, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero().item()) == 0
+
+
+# ------------------------------------------------------------------ distribution
+def test_gpu_lossless_marginal_chi_square(sv, orc):
+    """The GPU as a sampler over 10^6 sequences at V=8: every emitted token
+    follows the target distribution, and decisions match the oracle."""
+    from scipy import stats
+    from scipy.special import softmax
+    V, k, N, T = 8, 3, 10 ** 6, 1.0
+    rng = np.random.default_rng(11)
+    t = rng.standard_normal((k + 1, V)).astype(np.float32)
+    d = (t[:k] + 0.8 * rng.standard_normal((k, V))).astype(np.float32)
+    w = sv_inputs.fixed_rows(N, t, d, T, 11)
+    g = run_gpu(sv, w, aux=False)
+    p = softmax(t.astype(np.float64) / T, axis=1)
+    acc = g["accepted_len"]
+    for i in range(k + 1):
+        reach = acc >= i
+        counts = np.bincount(g["out_tokens"][reach, i], minlength=V)
+        _, pv = stats.chisquare(counts, p[i] * reach.sum())
+        assert pv > 1e-4 / (k + 1), (i, pv)
+    o = orc.verify_workload(w)
+    rep = compare_decisions(o, g, k)
+    assert not rep["fails"]
+    assert rep["exc_pos"] <= 0.001 * rep["positions"]
