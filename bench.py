@@ -1,0 +1,187 @@
+"""Benchmark of the speculative-sampling verification step on one MI355X.
+
+One step = one spec_verify call (acceptance chain, residual/bonus draw and
+top-32 for every verified position) over one batch of the steady-state rollout
+workload: B=32, k=3, V=151936, bf16 logits, T=1.  The inputs are synthetic and
+seeded; 16 copies of the batch (1.09 GB, over four times the 256 MB Infinity
+Cache) rotate so every step reads its logits from HBM.
+
+Prints one JSON line.  value = algorithmic logit bytes (each logit read once,
+B(2k+1)V * 2 bytes) / wall time per step, inputs resident in HBM.  roofline =
+the same bytes / the kernel's own duration (HIP events around each launch on
+the launch stream) against the 8 TB/s HBM peak.  cpu_baseline = the plain C
+oracle on the host over the same batch.
+
+  python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|tiny]
+  python bench.py --copy-calib    # a plain 1 GiB device copy, for HBM counter calibration
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "spec-verify logits GB/s (% HBM peak) + rows/s at B=32 k=3 V=151936 bf16"
+MALL_BYTES = 256 << 20
+
+
+def make_workload(name):
+    import sv_inputs
+    if name == "steady":
+        return sv_inputs.steady()
+    if name.startswith("longtail"):
+        return sv_inputs.longtail(int(name[len("longtail"):]))
+    if name == "grpo":
+        return sv_inputs.grpo()
+    if name == "wide":
+        return sv_inputs.wide()
+    if name == "wide_greedy":
+        return sv_inputs.wide(greedy=True)
+    if name == "tiny":
+        return sv_inputs.tiny()
+    raise SystemExit(f"unknown workload {name}")
+
+
+def describe(w):
+    return f"{w.name} B={w.B} k={w.k} V={w.V} {'bf16' if w.dtype else 'f32'} T={w.temperature:g}"
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The oracle as it stands, single-threaded, over whole batches until about
+    budget_s seconds have passed (at least one batch)."""
+    import oracle
+    oracle.build()
+    t0 = time.perf_counter()
+    n = 0
+    res = None
+    while True:
+        res = oracle.verify_workload(w)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return dt, n, res
+
+
+def copy_calib():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_per_launch_read": n, "write": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="steady")
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: enough for 4x the MALL)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verification step runs on a single MI355X "
+              "(sharding over B or V is a design note only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        return copy_calib()
+
+    import torch
+    import draft_verification_spec_amd as sv
+
+    w = make_workload(args.workload)
+    print(f"[bench] workload {describe(w)}", file=sys.stderr, flush=True)
+    t, d, x, u = sv.to_device(w)
+    greedy = w.temperature == 0
+    alg = w.alg_bytes()
+    copies = args.copies or max(1, -(-4 * MALL_BYTES // alg))
+    sets = [(t, d, x, u)] + [(t.clone(), d.clone(), x.clone(), u.clone()) for _ in range(copies - 1)]
+    shape = sv.make_shape(w.B, w.k, w.V, w.dtype, w.temperature)
+    ws = sv.workspace_for(t.device, sv.spec_verify_workspace_bytes(shape))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        tt, dd, xx, uu = sets[i % copies]
+        return sv.verify(tt, None if greedy else dd, xx, None if greedy else uu, w.temperature,
+                         workspace=ws, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps over {copies} input copies",
+          file=sys.stderr, flush=True)
+
+    # kernel duration: an event pair around each launch on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # whole-job wall time over K back-to-back steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    last = None
+    for i in range(args.steps):
+        last = step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    rows = w.B * (w.k + 1)
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    kern_avg = float(kern_ms.mean())
+    achieved = alg / (kern_avg * 1e-3) / 1e9
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in last._asdict().items()}
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype else "f32",
+        "data": "synthetic (seeded Philox logits of the workload's shape and distribution)",
+        "config": {"workload": describe(w), "B": w.B, "k": w.k, "V": w.V, "verified_rows": rows,
+                   "alg_bytes_per_step": alg, "input_copies_rotated": copies},
+        "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "spec_verify_kernel", "kernel_us_mean": round(kern_avg * 1e3, 3),
+                     "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, q)) * 1e3, 3) for q in (10, 50, 90)]},
+        "mean_accepted_len": float(np.mean(g["accepted_len"])),
+        "mean_accepted_len_plus1": float(np.mean(g["accepted_len"]) + 1),
+    }
+    if not args.no_cpu:
+        dt, n, o = cpu_baseline(w)
+        from tests.compare import compare_decisions   # same comparator as the parity tests
+        rep = compare_decisions(o, g, w.k) if not greedy else None
+        line["cpu_baseline"] = {
+            "value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {describe(w)} batch, {n} pass(es), {dt:.2f} s per batch, single thread of "
+                      f"{os.cpu_count()} host threads",
+            "rows_per_s": round(rows / dt, 2)}
+        if rep is not None:
+            line["parity_vs_oracle"] = {"fails": len(rep["fails"]), "exception_positions": rep["exc_pos"],
+                                        "positions": rep["positions"]}
+        else:
+            line["parity_vs_oracle"] = {"bit_exact": bool(np.array_equal(o["out_tokens"], g["out_tokens"]))}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,7 +51,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
 /* return codes (host-detected; nothing is launched when one is returned) */
 #define SV_OK 0
 #define SV_ERR_NULL (-1)        /* a required pointer is NULL */
-#define SV_ERR_SHAPE (-2)       /* B < 0, k < 0, V < 1, a row stride < V, or sizes too large */
+#define SV_ERR_SHAPE (-2)       /* B < 0, k < 0, V < 1, V above the maximum (524288 for bf16,
+                                   262144 for fp32), a row stride < V, or sizes too large */
 #define SV_ERR_TEMPERATURE (-3) /* temperature < 0, NaN or infinite */
 #define SV_ERR_DTYPE (-4)       /* dtype not SV_F32 / SV_BF16 */
 #define SV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than spec_verify_workspace_bytes */
@@ -69,7 +70,7 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
 typedef struct {
     int32_t B;                  /* sequences, >= 0 (0: nothing to do) */
     int32_t k;                  /* drafted tokens per sequence, >= 0 */
-    int32_t V;                  /* vocabulary size, >= 1 */
+    int32_t V;                  /* vocabulary size, 1 .. 524288 (bf16) or 262144 (fp32) */
     int32_t dtype;              /* sv_dtype_t of both logits tensors */
     int64_t target_row_stride;  /* elements between target rows (b,i) and (b,i+1), and
                                    between (b,k) and (b+1,0); 0 means V */

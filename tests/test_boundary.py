@@ -35,7 +35,10 @@ def test_workspace_bytes():
     assert big < 64 << 20                      # a few MB at the steady-state shape
     assert f(sv.make_shape(-1, 3, 10, 0, 1.0)) == 0
     assert f(sv.make_shape(1, 3, 0, 0, 1.0)) == 0
-    assert f(sv.make_shape(1, 3, (1 << 20) + 1, 0, 1.0)) == 0
+    assert f(sv.make_shape(1, 3, 262144, sv.SV_F32, 1.0)) > 0
+    assert f(sv.make_shape(1, 3, 262145, sv.SV_F32, 1.0)) == 0
+    assert f(sv.make_shape(1, 3, 524288, sv.SV_BF16, 1.0)) > 0
+    assert f(sv.make_shape(1, 3, 524289, sv.SV_BF16, 1.0)) == 0
     assert f(sv.make_shape(0, 3, 100, 0, 1.0)) > 0
 
 
@@ -57,6 +60,8 @@ def test_host_validation_codes():
     assert _call(sv.make_shape(-1, 3, 1000, 0, 1.0)) == sv.SV_ERR_SHAPE
     assert _call(sv.make_shape(2, -1, 1000, 0, 1.0)) == sv.SV_ERR_SHAPE
     assert _call(sv.make_shape(2, 3, 0, 0, 1.0)) == sv.SV_ERR_SHAPE
+    assert _call(sv.make_shape(2, 3, 262145, sv.SV_F32, 1.0)) == sv.SV_ERR_SHAPE
+    assert _call(sv.make_shape(2, 3, 524289, sv.SV_BF16, 1.0)) == sv.SV_ERR_SHAPE
     assert _call(sv.make_shape(2, 3, 1000, 0, 1.0, target_row_stride=999)) == sv.SV_ERR_SHAPE
     assert _call(sv.make_shape(2, 3, 1000, 0, 1.0, draft_row_stride=10)) == sv.SV_ERR_SHAPE
     assert _call(sv.make_shape(2, 3, 1000, 0, -1.0)) == sv.SV_ERR_TEMPERATURE
