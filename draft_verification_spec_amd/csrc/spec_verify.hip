@@ -1,37 +1,35 @@
 // spec_verify.hip -- speculative-sampling verification for gfx950 (MI355X).
 //
-// One persistent, cooperatively launched kernel runs the whole step.  The
-// vocabulary of every row is cut into fixed tiles (4096 entries for bf16, 2048
-// for fp32: 8 KB per row either way).  A work item is one tile of one "group":
-// for i < k the group is the pair (target row i, draft row i) of a sequence,
-// group k is target row k alone, and in greedy mode every group is one target
-// row.  Workgroups take items round-robin (item = blockIdx.x + r * gridDim.x);
-// the items of a group are consecutive, so a group is spread over distinct,
-// co-resident workgroups.  While a workgroup works on one item, the tiles of
-// its next item are already streaming into registers.
+// Two plain launches and no waiting between workgroups:
 //
-// Per item:
-//  A  stage the tile(s) in LDS (each thread keeps its own 16-byte vectors);
-//     per-thread max and sum of exp2((x - max) * log2(e)/T) (fp32 exp and
-//     per-thread fp32 sums, fp64 above the thread); reduce to a tile record and
-//     publish it.
-//  -- group barrier: wait until every tile of the group has published.
-//  B  combine the tile records in tile order (fp64) into the row max and
-//     normaliser, identical in every workgroup of the group; take the row's
-//     acceptance decision; write the tile's top-32 candidates (elements at or
-//     above the 32nd largest wave maximum of the row: at least 32 elements lie
-//     there) to the tile's slots.  If the row is the sequence's first rejection
-//     (or the bonus row after k acceptances), publish the tile's share of the
-//     residual mass max(0, p - q) (or of p).
-//  C  the last workgroup of the group merges the candidates into the top-32
-//     (value desc, index asc); the last group of the sequence assembles it: an
-//     inverse-CDF draw over the drawing row's tile masses in tile order, then
-//     the crossing tile re-read and scanned element by element.
+//  sv_stream  one workgroup per (group, tile).  A "group" is, for i < k, the
+//             pair (target row i, draft row i) of a sequence; group k is target
+//             row k alone; in greedy mode every group is one target row.  Tiles
+//             are fixed vocabulary slices (4096 entries for bf16, 2048 for fp32:
+//             8 KB per row either way).  Each workgroup streams its tile(s) once
+//             with 128-bit loads and publishes:
+//               - per-row-part max and sum of exp2((x - max) * log2(e)/T)
+//                 (fp32 exp, per-thread fp32 sums, fp64 above the thread);
+//               - the target tile's top-32 candidates: every element at or above
+//                 the tile's 32nd largest lane maximum (at least 32 elements of
+//                 the tile lie there, so the tile's top-32 is among them).
+//             The last workgroup of a group to publish combines the tile records
+//             in tile order into the row max and normaliser, takes the row's
+//             acceptance decision, and merges the candidates that reach the row
+//             bound (the largest tile bound) into the top-32 (value desc, index
+//             asc).  The last group of a sequence finds the first rejection j
+//             (or emits the greedy argmax-prefix result).
+//  sv_draw    sampling only: one workgroup per tile of the drawing row (row j's
+//             pair for a rejection, target row k after k acceptances) publishes
+//             the tile's residual mass max(0, p - q) (or p); the last one draws
+//             by inverse CDF over the tile masses in tile order and rescans the
+//             crossing tile element by element.
 //
-// Cross-workgroup data moves through the workspace with device-scope
-// write-through stores and device-scope loads, ordered by waiting for the
-// stores to complete before the counter that announces them is bumped.  No
-// L2 write-back or invalidate is needed anywhere.
+// Cross-workgroup data within a launch moves through the workspace with
+// device-scope write-through stores and device-scope loads, ordered by waiting
+// for the stores to complete before the counter that announces them is bumped.
+// No workgroup ever waits for another, so any launch order and any occupancy
+// are safe.
 //
 // Acceptance test, residual and bonus draw follow the ReSpec notes ("2 .
 // background": one-shot acceptance test Eq.1, residual max(0,p-q)/sum); the
@@ -44,8 +42,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "spec_verify.h"
 
 namespace {
@@ -53,11 +49,10 @@ namespace {
 constexpr int TPB = 256;               // threads per workgroup (4 waves of 64)
 constexpr int NWAVE = TPB / 64;
 constexpr int NSEG = 2;                // 16-byte vectors per thread per row
-constexpr int SLOTS = 32;              // top-32 candidate slots per tile
-constexpr int MERGE_CAP = 512;         // candidates a group merge ranks in LDS
+constexpr int SLOTS = 64;              // candidate slots per tile
+constexpr int MERGE_CAP = 512;         // candidates a row merge ranks in LDS
 constexpr int TOPK = SV_TOPK;
 constexpr int MAX_TILES = 128;
-constexpr uint32_t SPIN_LIMIT = 1u << 19;      // about half a second of polling
 constexpr float NEG_INF = -__builtin_inff();
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -66,27 +61,35 @@ template <int DT> struct Fmt;
 template <> struct Fmt<SV_BF16> { static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8; };
 template <> struct Fmt<SV_F32> { static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4; };
 
-// Published per (group, tile) after phase A.
+// Published per (group, tile) by sv_stream.
 struct TileRec {
   float m_t, m_d;          // tile max of the target / draft row part
   double s_t, s_d;         // sum exp2((x - m) * sc) over the tile part
-  uint32_t wkey[NWAVE];    // ordered key of each wave's target maximum, 0 = no element
+  uint32_t bound;          // ordered key of the tile's 32nd largest lane maximum (0: fewer lanes)
   int32_t flags_t, flags_d;
+  int32_t overflow;        // more candidates than SLOTS
+  uint32_t top[4];         // ordered keys of the tile's 4 largest lane maxima (0: no lane)
+  int32_t pad[2];
 };
 
-// Published per group by its tile-0 workgroup in phase B.
+// Published per group by its last workgroup.
 struct GroupRec {
   double s_t, s_d;         // row normalisers (relative to m_t, m_d)
   float m_t, m_d;          // row maxima
   int32_t flags;           // SV_STATUS_* bits of this group's rows and token
   int32_t accept;          // 1 when the drafted token passed (pair groups)
-  int32_t argmax;          // top-1 index of the target row (written by the merge)
+  int32_t argmax;          // top-1 index of the target row
   int32_t pad;
 };
 
-// arrive2 counts arrivals in its high half and candidate overflows in its low
-// half; dec: 0 pending, 1 drafted token accepted, 2 rejected or data error
-struct GroupSync { int32_t arrive1, arrive2, dec, pad; };
+// Handed from sv_stream to sv_draw per sequence (valid == 1: a token to draw).
+struct SeqRec {
+  double s_t, s_d;         // normalisers of the drawing row's target / draft part
+  float m_t, m_d;
+  int32_t j, valid;        // drawing position, and whether sv_draw has work
+  double u;                // the uniform of the draw
+  int32_t resid, pad;      // 1: residual of the pair row j; 0: target row k
+};
 
 struct Params {
   const char *target, *draft;
@@ -95,13 +98,14 @@ struct Params {
   const float *uniforms;
   int32_t *accepted_len, *out_tokens, *topk_idx, *status;
   float *topk_val, *lse_t, *lse_d, *p_tok, *q_tok;
-  GroupSync *sync;
-  int32_t *seqctr, *fault;
+  int32_t *fault;                      // set when the workspace was not zero-filled
+  int32_t *garrive, *sarrive, *darrive;
   TileRec *recs;
-  double *rsum;
   GroupRec *grec;
+  SeqRec *srec;
   uint64_t *cand;                      // [group][tile][SLOTS] candidate keys, 0 = empty
-  int32_t B, k, V, nT, items;
+  double *rsum;                        // [sequence][tile] masses of the drawing row
+  int32_t B, k, V, nT;
   float T, sc;                         // sc = log2(e) / T
   double scd;
   int32_t t_vec, d_vec;                // rows 16-byte aligned
@@ -109,17 +113,15 @@ struct Params {
 
 struct Smem {
   union {
-    u32x4 tile[2][NSEG][TPB];          // staged tile: [target, draft][vector][thread]
-    uint64_t keys[MERGE_CAP];          // group merge: candidate keys
+    uint32_t lists[NWAVE][32];         // per-wave top-32 lane maxima
+    uint32_t tops[4 * MAX_TILES];      // row merge: the tiles' largest lane maxima
+    uint64_t keys[MERGE_CAP];          // row merge: candidate keys
     struct {                           // exact top-32 fallback
       uint32_t hist[2048];
       int32_t part[TPB];
       uint64_t list[TOPK];
     } fb;
-  };
-  union {
-    uint32_t wkeys[NWAVE * MAX_TILES]; // phase B: wave maxima of the row
-    double tot[MAX_TILES];             // sequence assembly: tile masses
+    double tot[MAX_TILES];             // draw: tile masses
   };
   float f[4][NWAVE];
   uint32_t u[2][NWAVE];
@@ -127,6 +129,7 @@ struct Smem {
   double d[4][NWAVE];
   int32_t bc[8];
   double dbc[4];
+  uint64_t ovmask[NWAVE];              // row merge: tiles whose candidates overflowed
 };
 
 // ---------------------------------------------------------------- helpers
@@ -185,6 +188,20 @@ __device__ __forceinline__ double wave_incl_dbl(double v, int lane) {
   for (int d = 1; d < 64; d <<= 1) { double w = __shfl_up(v, d); if (lane >= d) v += w; }
   return v;
 }
+// Bitonic sort of one value per lane, descending across the wave's 64 lanes.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t o = __shfl_xor(v, j);
+      const bool desc = (lane & k) == 0, lower = (lane & j) == 0;
+      const uint32_t hi = v > o ? v : o, lo = v > o ? o : v;
+      v = (lower == desc) ? hi : lo;
+    }
+  }
+  return v;
+}
 
 // Device-scope accesses: loads see the latest device-visible value; stores are
 // written through to the device coherence point.  No cache maintenance.
@@ -203,6 +220,17 @@ __device__ __forceinline__ void stores_done() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+// Announce this workgroup's published data on a counter; returns the count
+// before it (the same value in every thread).
+__device__ __forceinline__ int arrive(int32_t *ctr, Smem &sm) {
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) sm.bc[7] = add_dev(ctr, 1);
+  __syncthreads();
+  const int old = sm.bc[7];
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return old;
 }
 // Records move as 64-bit words.
 template <class T> __device__ __forceinline__ void st_rec(T *dst, const T &v) {
@@ -225,19 +253,6 @@ template <class T> __device__ __forceinline__ void zero_recs(T *dst, int n) {
   uint64_t *d = (uint64_t *)dst;
   const int words = n * (int)(sizeof(T) / 8);
   for (int w = threadIdx.x; w < words; w += TPB) st_dev(d + w, (uint64_t)0);
-}
-// Poll a device counter until it reaches `target`.  A wait that never ends
-// would be a bug: after SPIN_LIMIT polls (or once another wait has given up)
-// mark the fault word and return, so the grid always drains.
-__device__ __forceinline__ void wait_at_least(const int32_t *p, int target, int32_t *fault) {
-  uint32_t spins = 0;
-  while (ld_dev(p) < target) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++spins > SPIN_LIMIT || ((spins & 255) == 0 && ld_dev(fault))) {
-      atomicOr(fault, 1);
-      return;
-    }
-  }
 }
 
 template <int DT> __device__ __forceinline__ float load_elem(const char *row, int64_t x) {
@@ -292,61 +307,21 @@ __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool ve
   }
 }
 
-struct Geo {
-  int g, c, b, i;
-  bool pair;
-  const char *trow, *drow;
-};
-
-template <int DT, bool GREEDY> __device__ __forceinline__ Geo geo(const Params &P, int item) {
-  Geo G;
-  const int K1 = P.k + 1;
-  G.g = item / P.nT;
-  G.c = item - G.g * P.nT;
-  G.b = G.g / K1;
-  G.i = G.g - G.b * K1;
-  G.pair = !GREEDY && G.i < P.k;
-  G.trow = P.target + ((int64_t)G.b * K1 + G.i) * P.tstride * Fmt<DT>::E;
-  G.drow = G.pair ? P.draft + ((int64_t)G.b * P.k + G.i) * P.dstride * Fmt<DT>::E : nullptr;
-  return G;
-}
-
-template <int DT, bool GREEDY>
-__device__ __forceinline__ void fetch(const Params &P, int item, u32x4 (&nt)[NSEG], u32x4 (&nd)[NSEG]) {
-  const Geo G = geo<DT, GREEDY>(P, item);
-  load_tile<DT>(G.trow, G.c, P.V, P.t_vec, nt);
-  if (G.pair) load_tile<DT>(G.drow, G.c, P.V, P.d_vec, nd);
-}
-
-// Each thread stages its own vectors and only ever reads those back, so no
-// barrier is needed between staging and use.
-__device__ __forceinline__ void stage(Smem &sm, const u32x4 (&t)[NSEG], const u32x4 (&d)[NSEG], bool pair) {
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    sm.tile[0][s][threadIdx.x] = t[s];
-    if (pair) sm.tile[1][s][threadIdx.x] = d[s];
-  }
-}
-
-template <int DT> __device__ __forceinline__ float thread_max(const Smem &sm, int r) {
+template <int DT> __device__ __forceinline__ float thread_max(const u32x4 (&r)[NSEG]) {
   float m = NEG_INF;
 #pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    const u32x4 v = sm.tile[r][s][threadIdx.x];
+  for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) m = fmaxf(m, unpack<DT>(v, w));
-  }
+    for (int w = 0; w < Fmt<DT>::W; ++w) m = fmaxf(m, unpack<DT>(r[s], w));
   return m;
 }
 
-template <int DT> __device__ __forceinline__ bool thread_has_nan(const Smem &sm, int r) {
+template <int DT> __device__ __forceinline__ bool thread_has_nan(const u32x4 (&r)[NSEG]) {
   bool nan = false;
 #pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    const u32x4 v = sm.tile[r][s][threadIdx.x];
+  for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) { const float x = unpack<DT>(v, w); nan |= !(x == x); }
-  }
+    for (int w = 0; w < Fmt<DT>::W; ++w) { const float x = unpack<DT>(r[s], w); nan |= !(x == x); }
   return nan;
 }
 
@@ -358,16 +333,14 @@ __device__ __forceinline__ float scaled_exp(float x, float m, float sc) {
 
 // Sequential fp32 sum of the thread's scaled exps; flags NaN / +inf.
 template <int DT>
-__device__ __forceinline__ float thread_expsum(const Smem &sm, int r, float m, float sc, int &flags) {
+__device__ __forceinline__ float thread_expsum(const u32x4 (&r)[NSEG], float m, float sc, int &flags) {
   float s = 0.f;
 #pragma unroll
-  for (int g = 0; g < NSEG; ++g) {
-    const u32x4 v = sm.tile[r][g][threadIdx.x];
+  for (int g = 0; g < NSEG; ++g)
 #pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) s += scaled_exp(unpack<DT>(v, w), m, sc);
-  }
+    for (int w = 0; w < Fmt<DT>::W; ++w) s += scaled_exp(unpack<DT>(r[g], w), m, sc);
   flags = 0;
-  if (!(s == s)) flags = thread_has_nan<DT>(sm, r) ? SV_STATUS_NAN : SV_STATUS_POSINF;
+  if (!(s == s)) flags = thread_has_nan<DT>(r) ? SV_STATUS_NAN : SV_STATUS_POSINF;
   return s;
 }
 
@@ -388,17 +361,15 @@ __device__ __forceinline__ float elem_mass(const u32x4 &vt, const u32x4 &vd, int
   return r > 0.f ? r : 0.f;
 }
 
-// Sequential fp32 mass of each of the thread's vectors of the staged tile.
+// Sequential fp32 mass of each of the thread's vectors.
 template <int DT>
-__device__ __forceinline__ void seg_masses(const Smem &sm, bool resid, float mt, float md, float at, float ad,
-                                           float sc, float (&seg)[NSEG]) {
+__device__ __forceinline__ void seg_masses(const u32x4 (&rt)[NSEG], const u32x4 (&rd)[NSEG], bool resid, float mt,
+                                           float md, float at, float ad, float sc, float (&seg)[NSEG]) {
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
-    const u32x4 vt = sm.tile[0][s][threadIdx.x];
-    const u32x4 vd = resid ? sm.tile[1][s][threadIdx.x] : vt;
     float a = 0.f;
 #pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) a += elem_mass<DT>(vt, vd, w, resid, mt, md, at, ad, sc);
+    for (int w = 0; w < Fmt<DT>::W; ++w) a += elem_mass<DT>(rt[s], rd[s], w, resid, mt, md, at, ad, sc);
     seg[s] = a;
   }
 }
@@ -429,8 +400,21 @@ __device__ double tile_scan(const float (&seg)[NSEG], double (&base)[NSEG], Smem
   return acc;
 }
 
+// Block-wide OR and MIN through LDS.
+__device__ __forceinline__ void block_or_min(int &o, int &m, Smem &sm) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  o = wave_or(o);
+  m = wave_min_i(m);
+  if (lane == 0) { sm.i[0][wid] = o; sm.i[1][wid] = m; }
+  __syncthreads();
+  o = sm.i[0][0];
+  m = sm.i[1][0];
+  for (int w = 1; w < NWAVE; ++w) { o |= sm.i[0][w]; m = sm.i[1][w] < m ? sm.i[1][w] : m; }
+  __syncthreads();
+}
+
 // Top-32 of a target row by exact radix selection over the whole row (used
-// when the candidate slots overflowed).  Rank 0's index goes to sm.bc[7].
+// when the candidate slots overflowed).  Rank 0's index goes to sm.bc[6].
 template <int DT>
 __device__ void topk_exact(const char *row, int V, float *oval, int32_t *oidx, Smem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -511,37 +495,159 @@ __device__ void topk_exact(const char *row, int V, float *oval, int32_t *oidx, S
     for (int j = 0; j < need; ++j) rank += sm.fb.list[j] > ka;
     oidx[rank] = cand_index(ka);
     oval[rank] = cand_value(ka);
-    if (rank == 0) sm.bc[7] = cand_index(ka);
+    if (rank == 0) sm.bc[6] = cand_index(ka);
   }
   for (int r = need + tid; r < TOPK; r += TPB) { oidx[r] = -1; oval[r] = NEG_INF; }
   __syncthreads();
 }
 
-// Top-32 of a target row from the candidate slots of its tiles (the last
-// workgroup of the group runs it).  Every slot read non-empty is cleared.
-template <int DT>
-__device__ void merge_top32(const Params &P, int g, int row, bool overflow, bool nanrow, const char *trow,
-                            Smem &sm) {
-  const int tid = threadIdx.x;
-  float *oval = P.topk_val + (int64_t)row * TOPK;
-  int32_t *oidx = P.topk_idx + (int64_t)row * TOPK;
-  if (tid == 0) { sm.bc[6] = 0; sm.bc[7] = -1; }
-  __syncthreads();
-  uint64_t *slots = P.cand + (int64_t)g * P.nT * SLOTS;
-  for (int a = tid; a < P.nT * SLOTS; a += TPB) {
-    const uint64_t key = ld_dev(slots + a);
-    if (key) {
-      st_dev(slots + a, (uint64_t)0);
-      const int pos = atomicAdd(&sm.bc[6], 1);
-      if (pos < MERGE_CAP) sm.keys[pos] = key;
+struct Geo {
+  int g, c, b, i;
+  bool pair;
+  const char *trow, *drow;
+};
+
+template <int DT, bool GREEDY> __device__ __forceinline__ Geo geo(const Params &P, int item) {
+  Geo G;
+  const int K1 = P.k + 1;
+  G.g = item / P.nT;
+  G.c = item - G.g * P.nT;
+  G.b = G.g / K1;
+  G.i = G.g - G.b * K1;
+  G.pair = !GREEDY && G.i < P.k;
+  G.trow = P.target + ((int64_t)G.b * K1 + G.i) * P.tstride * Fmt<DT>::E;
+  G.drow = G.pair ? P.draft + ((int64_t)G.b * P.k + G.i) * P.dstride * Fmt<DT>::E : nullptr;
+  return G;
+}
+
+// Row combine, acceptance decision and top-32 merge of group g (run by the
+// last workgroup of the group to publish).
+template <int DT, bool GREEDY>
+__device__ void group_finish(const Params &P, const Geo &G, Smem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nT = P.nT, k = P.k, K1 = k + 1, V = P.V;
+  const int g = G.g, b = G.b, i = G.i;
+  const bool pair = G.pair;
+  // the tile records (nT <= TPB: thread cc holds tile cc) and the drafted token's logits
+  TileRec rec;
+  const bool own = tid < nT;
+  if (own) {
+    rec = ld_rec(P.recs + (int64_t)g * nT + tid);
+  } else {
+    rec.m_t = NEG_INF; rec.m_d = NEG_INF; rec.s_t = 0.0; rec.s_d = 0.0;
+    rec.bound = 0; rec.flags_t = 0; rec.flags_d = 0; rec.overflow = 0;
+    for (int w = 0; w < 4; ++w) rec.top[w] = 0;
+  }
+  if (own)
+    for (int w = 0; w < 4; ++w) sm.tops[tid * 4 + w] = rec.top[w];
+  int32_t x = -1;
+  float tx = 0.f, dx = 0.f;
+  if (pair && tid == 0) {
+    x = P.tokens[(int64_t)b * k + i];
+    if (x >= 0 && x < V) { tx = load_elem<DT>(G.trow, x); dx = load_elem<DT>(G.drow, x); }
+  }
+  {
+    const float a = wave_max(rec.m_t), d = wave_max(rec.m_d);
+    const int fa = wave_or(rec.flags_t), fb = wave_or(rec.flags_d);
+    const uint32_t bd = wave_max_u(rec.bound);
+    const uint64_t ov = __ballot(own && rec.overflow);
+    if (lane == 0) {
+      sm.f[2][wid] = a; sm.f[3][wid] = d; sm.i[2][wid] = fa; sm.i[3][wid] = fb; sm.u[1][wid] = bd;
+      sm.ovmask[wid] = ov;
     }
   }
   __syncthreads();
-  const int n = sm.bc[6];
-  if (nanrow) {
+  float m_rt = sm.f[2][0], m_rd = sm.f[3][0];
+  int f_rt = sm.i[2][0], f_rd = sm.i[3][0];
+  uint32_t L = sm.u[1][0];
+  for (int w = 1; w < NWAVE; ++w) {
+    m_rt = fmaxf(m_rt, sm.f[2][w]); m_rd = fmaxf(m_rd, sm.f[3][w]);
+    f_rt |= sm.i[2][w]; f_rd |= sm.i[3][w];
+    L = sm.u[1][w] > L ? sm.u[1][w] : L;
+  }
+  double s_rt = 0.0, s_rd = 0.0;
+  if (!GREEDY) {
+    double a = 0.0, d = 0.0;
+    if (own && rec.m_t != NEG_INF) a = rec.s_t * (double)__builtin_amdgcn_exp2f((rec.m_t - m_rt) * P.sc);
+    if (own && pair && rec.m_d != NEG_INF) d = rec.s_d * (double)__builtin_amdgcn_exp2f((rec.m_d - m_rd) * P.sc);
+    a = wave_sum(a);
+    d = wave_sum(d);
+    if (lane == 0) { sm.d[2][wid] = a; sm.d[3][wid] = d; }
+    __syncthreads();
+    for (int w = 0; w < NWAVE; ++w) { s_rt += sm.d[2][w]; s_rd += sm.d[3][w]; }
+  }
+  // one data-error bit per row: NaN before +inf before an empty row
+  f_rt = (f_rt & SV_STATUS_NAN) ? SV_STATUS_NAN : f_rt;
+  f_rd = (f_rd & SV_STATUS_NAN) ? SV_STATUS_NAN : f_rd;
+  if (!GREEDY && m_rt == NEG_INF && !f_rt) f_rt = SV_STATUS_EMPTY_ROW;
+  if (pair && m_rd == NEG_INF && !f_rd) f_rd = SV_STATUS_EMPTY_ROW;
+
+  // A tighter row bound: the 32nd largest of the tiles' 4 largest lane maxima
+  // (32 distinct lanes hold an element at or above it).  The row's 32nd
+  // largest element is at or above both bounds, and every element at or above
+  // L sits in its tile's slots.
+  if (wid == 0) {
+    const int nkeys = nT * 4;
+    uint32_t prefix = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      int cnt = 0;
+      for (int j0 = 0; j0 < nkeys; j0 += 64) {
+        const int jj = j0 + lane;
+        cnt += __popcll(__ballot(jj < nkeys && sm.tops[jj] >= cand));
+      }
+      if (cnt >= TOPK) prefix = cand;
+    }
+    if (lane == 0) sm.u[0][0] = prefix;
+  }
+  __syncthreads();
+  L = sm.u[0][0] > L ? sm.u[0][0] : L;
+  // candidates reaching the row bound; every non-empty slot is cleared.  A tile
+  // that had more candidates than slots is rescanned here against the bound.
+  if (tid == 0) { sm.bc[0] = 0; sm.bc[6] = -1; }
+  __syncthreads();
+  uint64_t *slots = P.cand + (int64_t)g * nT * SLOTS;
+  for (int a = tid; a < nT * SLOTS; a += TPB) {
+    const uint64_t key = ld_dev(slots + a);
+    if (key) {
+      st_dev(slots + a, (uint64_t)0);
+      const int tc = a / SLOTS;
+      const bool ovf = (sm.ovmask[tc >> 6] >> (tc & 63)) & 1u;
+      if (!ovf && (uint32_t)(key >> 32) >= L) {
+        const int pos = atomicAdd(&sm.bc[0], 1);
+        if (pos < MERGE_CAP) sm.keys[pos] = key;
+      }
+    }
+  }
+  for (int wq = 0; wq < NWAVE; ++wq) {
+    uint64_t m = sm.ovmask[wq];
+    while (m) {
+      const int tc = wq * 64 + __builtin_ctzll(m);
+      m &= m - 1;
+      u32x4 r[NSEG];
+      load_tile<DT>(G.trow, tc, V, P.t_vec, r);
+      const int lim = V - tc * Fmt<DT>::TILE;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+        for (int w = 0; w < Fmt<DT>::W; ++w) {
+          const float xv = unpack<DT>(r[s], w);
+          if (tpos<DT>(s, w) < lim && xv == xv && ordered_key(xv) >= L) {
+            const int pos = atomicAdd(&sm.bc[0], 1);
+            if (pos < MERGE_CAP) sm.keys[pos] = cand_key(xv, tc * Fmt<DT>::TILE + tpos<DT>(s, w));
+          }
+        }
+    }
+  }
+  __syncthreads();
+  const int n = sm.bc[0];
+  const bool overflow = false;
+  float *oval = P.topk_val + ((int64_t)b * K1 + i) * TOPK;
+  int32_t *oidx = P.topk_idx + ((int64_t)b * K1 + i) * TOPK;
+  if (f_rt & SV_STATUS_NAN) {
     for (int r = tid; r < TOPK; r += TPB) { oval[r] = __builtin_nanf(""); oidx[r] = -1; }
   } else if (overflow || n > MERGE_CAP) {
-    topk_exact<DT>(trow, P.V, oval, oidx, sm);
+    topk_exact<DT>(G.trow, V, oval, oidx, sm);
   } else {
     for (int a = tid; a < n; a += TPB) {
       const uint64_t ka = sm.keys[a];
@@ -550,53 +656,257 @@ __device__ void merge_top32(const Params &P, int g, int row, bool overflow, bool
       if (rank < TOPK) {
         oidx[rank] = cand_index(ka);
         oval[rank] = cand_value(ka);
-        if (rank == 0) sm.bc[7] = cand_index(ka);
+        if (rank == 0) sm.bc[6] = cand_index(ka);
       }
     }
     for (int r = n + tid; r < TOPK; r += TPB) { oval[r] = NEG_INF; oidx[r] = -1; }
   }
   __syncthreads();
+
+  // acceptance decision of the row; the group record for the sequence
+  if (tid == 0) {
+    int fl = GREEDY ? (f_rt & SV_STATUS_NAN) : (f_rt | (pair ? f_rd : 0));
+    int acc = 1;
+    float pt = __builtin_nanf(""), qt = __builtin_nanf("");
+    if (pair) {
+      if (x < 0 || x >= V) {
+        fl |= SV_STATUS_BAD_TOKEN;
+        acc = 0;
+      } else if (!fl) {
+        const double p = exp2(((double)tx - (double)m_rt) * P.scd) / s_rt;
+        const double q = exp2(((double)dx - (double)m_rd) * P.scd) / s_rd;
+        const double ratio = q > 0.0 ? p / q : (p > 0.0 ? __builtin_inf() : 0.0);
+        const double a = ratio < 1.0 ? ratio : 1.0;
+        const double u = (double)P.uniforms[(int64_t)b * (k + 2) + i];
+        acc = (u < a) ? 1 : 0;
+        pt = (float)p;
+        qt = (float)q;
+      } else {
+        acc = 0;
+      }
+    }
+    GroupRec gr;
+    gr.s_t = s_rt; gr.s_d = s_rd; gr.m_t = m_rt; gr.m_d = m_rd;
+    gr.flags = fl; gr.accept = acc; gr.argmax = sm.bc[6]; gr.pad = 0;
+    st_rec(P.grec + g, gr);
+    if (!GREEDY) {
+      if (P.lse_t) P.lse_t[(int64_t)b * K1 + i] = (float)((double)m_rt / (double)P.T + log(s_rt));
+      if (pair) {
+        if (P.p_tok) P.p_tok[(int64_t)b * k + i] = pt;
+        if (P.q_tok) P.q_tok[(int64_t)b * k + i] = qt;
+        if (P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)m_rd / (double)P.T + log(s_rd));
+      }
+    }
+  }
+  // every workgroup of the group has published and left: clear the group
+  zero_recs(P.recs + (int64_t)g * nT, nT);
+  if (tid == 0) st_dev(P.garrive + g, 0);
 }
 
-// Stage tile c of a row (and of the draft row when resid) and compute the
-// per-thread scales; same arithmetic as the row's own items used.
-template <int DT>
-__device__ __forceinline__ void stage_row_tile(const Params &P, const char *trow, const char *drow, int c, bool resid,
-                                               float m_t, double s_t, float m_d, double s_d, Smem &sm, float &mt,
-                                               float &md, float &at, float &ad) {
+// Sequence assembly in sv_stream (run by the last group of the sequence):
+// greedy emits everything; sampling emits all but the drawn token and hands
+// the drawing row to sv_draw.
+template <bool GREEDY>
+__device__ void seq_finish(const Params &P, int b, Smem &sm) {
+  const int tid = threadIdx.x;
+  const int k = P.k, K1 = k + 1;
+  int st = 0, j = k;
+  for (int i = tid; i <= k; i += TPB) {
+    const GroupRec r = ld_rec(P.grec + (int64_t)b * K1 + i);
+    st |= r.flags;
+    if (i < k) {
+      if (GREEDY) {
+        const int32_t x = P.tokens[(int64_t)b * k + i];
+        if (x < 0 || x >= P.V) st |= SV_STATUS_BAD_TOKEN;
+        else if (x != r.argmax && i < j) j = i;
+      } else if (!r.accept && i < j) {
+        j = i;
+      }
+    }
+  }
+  if (!GREEDY)
+    for (int i = tid; i < k + 2; i += TPB) {
+      const float u = P.uniforms[(int64_t)b * (k + 2) + i];
+      if (!(u >= 0.f && u < 1.f)) st |= SV_STATUS_BAD_UNIFORM;
+    }
+  if (tid == 0 && ld_dev(P.fault)) st |= SV_STATUS_SYNC_TIMEOUT;
+  block_or_min(st, j, sm);
+  if (tid == 0) {
+    if (P.status) P.status[b] = st;
+    P.accepted_len[b] = st ? -1 : j;
+    const GroupRec rj = ld_rec(P.grec + (int64_t)b * K1 + j);
+    if (GREEDY) {
+      sm.bc[1] = rj.argmax;
+    } else if (!st) {
+      SeqRec sr;
+      sr.s_t = rj.s_t; sr.s_d = rj.s_d; sr.m_t = rj.m_t; sr.m_d = rj.m_d;
+      sr.j = j; sr.valid = 1;
+      sr.u = (double)P.uniforms[(int64_t)b * (k + 2) + (j < k ? k : k + 1)];
+      sr.resid = j < k ? 1 : 0; sr.pad = 0;
+      P.srec[b] = sr;                  // read by sv_draw after this launch
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < K1; i += TPB) {
+    int v = -1;
+    if (!st && i < j) v = P.tokens[(int64_t)b * k + i];
+    if (!st && i == j && GREEDY) v = sm.bc[1];
+    if (st || i != j || GREEDY) P.out_tokens[(int64_t)b * K1 + i] = v;
+  }
+  __syncthreads();
+  zero_recs(P.grec + (int64_t)b * K1, K1);
+  if (tid == 0) st_dev(P.sarrive + b, 0);
+}
+
+template <int DT, bool GREEDY>
+__global__ __launch_bounds__(TPB) void sv_stream(Params P) {
+  __shared__ Smem sm;
+  constexpr int W = Fmt<DT>::W, TILE = Fmt<DT>::TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nT = P.nT, V = P.V;
+  const int item = blockIdx.x;
+  const Geo G = geo<DT, GREEDY>(P, item);
+  const int g = G.g, c = G.c;
+  const bool pair = G.pair;
+
   u32x4 rt[NSEG], rd[NSEG];
-  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
-  if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
-  __syncthreads();               // the staging area may still hold another use's data
-  stage(sm, rt, rd, resid);
-  mt = thread_max<DT>(sm, 0);
-  md = resid ? thread_max<DT>(sm, 1) : NEG_INF;
-  at = prob_scale(mt, m_t, s_t, P.sc);
-  ad = resid ? prob_scale(md, m_d, s_d, P.sc) : 0.f;
+  load_tile<DT>(G.trow, c, V, P.t_vec, rt);
+  if (pair) load_tile<DT>(G.drow, c, V, P.d_vec, rd);
+  else
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
+
+  // per-thread statistics
+  const float mt = thread_max<DT>(rt);
+  const float md = pair ? thread_max<DT>(rd) : NEG_INF;
+  int ft = 0, fd = 0;
+  float st = 0.f, sd = 0.f;
+  if (!GREEDY) {
+    st = thread_expsum<DT>(rt, mt, P.sc, ft);
+    if (pair) sd = thread_expsum<DT>(rd, md, P.sc, fd);
+  } else {
+    ft = thread_has_nan<DT>(rt) ? SV_STATUS_NAN : 0;
+  }
+  const bool has_elem = (int64_t)c * TILE + (int64_t)tid * W < V;
+  const uint32_t tkey = has_elem ? ordered_key(mt) : 0u;
+
+  // per-wave top-32 lane maxima, tile max and flags
+  const uint32_t sorted = wave_sort_desc(tkey, lane);
+  if (lane < 32) sm.lists[wid][lane] = sorted;
+  {
+    const float wm_t = wave_max(mt), wm_d = wave_max(md);
+    const int wf_t = wave_or(ft), wf_d = wave_or(fd);
+    if (lane == 0) { sm.f[0][wid] = wm_t; sm.f[1][wid] = wm_d; sm.i[0][wid] = wf_t; sm.i[1][wid] = wf_d; }
+  }
+  __syncthreads();
+  // the tile bound: 32nd largest of the 256 lane maxima (top 32 of each pair
+  // of sorted lists merged, then sorted)
+  if (wid == 0) {
+    const int h = lane & 31;
+    const uint32_t p = lane < 32 ? sm.lists[0][h] : sm.lists[2][h];
+    const uint32_t q = lane < 32 ? sm.lists[1][31 - h] : sm.lists[3][31 - h];
+    const uint32_t s2 = wave_sort_desc(p > q ? p : q, lane);
+    const uint32_t b32 = __shfl(s2, 31);
+    if (lane == 0) sm.u[0][0] = b32;
+    if (lane < 4) sm.u[1][lane] = s2;
+  }
+  float m_ct = sm.f[0][0], m_cd = sm.f[1][0];
+  int f_ct = sm.i[0][0], f_cd = sm.i[1][0];
+  for (int w = 1; w < NWAVE; ++w) {
+    m_ct = fmaxf(m_ct, sm.f[0][w]); m_cd = fmaxf(m_cd, sm.f[1][w]);
+    f_ct |= sm.i[0][w]; f_cd |= sm.i[1][w];
+  }
+  if (!GREEDY) {
+    double a = (mt == NEG_INF) ? 0.0 : (double)st * (double)__builtin_amdgcn_exp2f((mt - m_ct) * P.sc);
+    double d = 0.0;
+    if (pair) d = (md == NEG_INF) ? 0.0 : (double)sd * (double)__builtin_amdgcn_exp2f((md - m_cd) * P.sc);
+    a = wave_sum(a);
+    d = wave_sum(d);
+    if (lane == 0) { sm.d[0][wid] = a; sm.d[1][wid] = d; }
+  }
+  __syncthreads();
+  double s_ct = 0.0, s_cd = 0.0;
+  if (!GREEDY) for (int w = 0; w < NWAVE; ++w) { s_ct += sm.d[0][w]; s_cd += sm.d[1][w]; }
+  const uint32_t bound = sm.u[0][0];
+
+  // candidates: elements at or above the bound, to this tile's slots in element order
+  int overflow = 0;
+  {
+    const float Lf = key_value(bound);
+    const int lim = V - c * TILE;                        // tile positions < lim exist
+    uint32_t mask = 0;
+    if (has_elem && (bound == 0u || mt >= Lf)) {
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          const float xv = unpack<DT>(rt[s], w);
+          if (tpos<DT>(s, w) < lim && (bound == 0u || xv >= Lf)) mask |= 1u << (s * W + w);
+        }
+    }
+    const int cnt = __popc(mask);
+    const int inc = wave_incl_int(cnt, lane);
+    if (lane == 63) sm.i[2][wid] = inc;
+    __syncthreads();
+    int slot = inc - cnt, total = 0;
+    for (int w = 0; w < NWAVE; ++w) { if (w < wid) slot += sm.i[2][w]; total += sm.i[2][w]; }
+    uint64_t *dst = P.cand + ((int64_t)g * nT + c) * SLOTS;
+    while (mask) {
+      const int bit = __builtin_ctz(mask);
+      mask &= mask - 1;
+      const int s = bit / W, w = bit - s * W;
+      if (slot < SLOTS) st_dev(dst + slot, cand_key(unpack<DT>(rt[s], w), c * TILE + tpos<DT>(s, w)));
+      ++slot;
+    }
+    overflow = total > SLOTS ? 1 : 0;
+  }
+
+  if (tid == 0) {
+    TileRec r;
+    r.m_t = m_ct; r.m_d = m_cd; r.s_t = s_ct; r.s_d = s_cd;
+    r.bound = bound; r.flags_t = f_ct; r.flags_d = f_cd; r.overflow = overflow;
+    for (int w = 0; w < 4; ++w) r.top[w] = sm.u[1][w];
+    r.pad[0] = 0; r.pad[1] = 0;
+    st_rec(P.recs + item, r);
+  }
+  const int old = arrive(P.garrive + g, sm);
+  if (old < 0 || old >= nT) { if (tid == 0) atomicOr(P.fault, 2); return; }  // workspace not zero-filled
+  if (old != nT - 1) return;
+  group_finish<DT, GREEDY>(P, G, sm);
+  const int olds = arrive(P.sarrive + G.b, sm);
+  if (olds != P.k) return;
+  seq_finish<GREEDY>(P, G.b, sm);
 }
 
-// Draw by inverse CDF inside one tile: the first element (ascending index) of
+// Inverse-CDF draw inside one tile: the first element (ascending index) of
 // positive mass whose cumulative mass prefix + (scan base + running fp32 sum)
 // exceeds tau; if rounding leaves none, the tile's last positive-mass element.
+// The masses are recomputed exactly as when the tile's total was published.
 template <int DT>
 __device__ int tile_draw(const Params &P, const char *trow, const char *drow, int c, bool resid, float m_t,
                          double s_t, float m_d, double s_d, double prefix, double tau, Smem &sm) {
   constexpr int W = Fmt<DT>::W;
-  float mt, md, at, ad;
-  stage_row_tile<DT>(P, trow, drow, c, resid, m_t, s_t, m_d, s_d, sm, mt, md, at, ad);
+  u32x4 rt[NSEG], rd[NSEG];
+  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
+  if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
+  else
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
+  const float mt = thread_max<DT>(rt);
+  const float md = resid ? thread_max<DT>(rd) : NEG_INF;
+  const float at = prob_scale(mt, m_t, s_t, P.sc);
+  const float ad = resid ? prob_scale(md, m_d, s_d, P.sc) : 0.f;
   float seg[NSEG];
-  seg_masses<DT>(sm, resid, mt, md, at, ad, P.sc, seg);
+  seg_masses<DT>(rt, rd, resid, mt, md, at, ad, P.sc, seg);
   double base[NSEG];
   tile_scan(seg, base, sm);
   int first = 0x7fffffff, lastpos = -1;
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
-    const u32x4 vt = sm.tile[0][s][threadIdx.x];
-    const u32x4 vd = resid ? sm.tile[1][s][threadIdx.x] : vt;
     float a = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const float mval = elem_mass<DT>(vt, vd, w, resid, mt, md, at, ad, P.sc);
+      const float mval = elem_mass<DT>(rt[s], rd[s], w, resid, mt, md, at, ad, P.sc);
       a += mval;
       const int pos = tpos<DT>(s, w);
       if (mval > 0.f) {
@@ -623,427 +933,100 @@ __device__ int tile_draw(const Params &P, const char *trow, const char *drow, in
   return pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
 }
 
-// Target mass p of one tile (same arithmetic as tile_draw without a draft row).
+// Total target mass p of one tile (the arithmetic of tile_draw without a draft row).
 template <int DT>
 __device__ double tile_mass_p(const Params &P, const char *trow, int c, float m_t, double s_t, Smem &sm) {
-  float mt, md, at, ad;
-  stage_row_tile<DT>(P, trow, nullptr, c, false, m_t, s_t, 0.f, 1.0, sm, mt, md, at, ad);
+  u32x4 rt[NSEG];
+  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
+  const float mt = thread_max<DT>(rt);
+  const float at = prob_scale(mt, m_t, s_t, P.sc);
   float seg[NSEG];
-  seg_masses<DT>(sm, false, mt, md, at, ad, P.sc, seg);
+  seg_masses<DT>(rt, rt, false, mt, NEG_INF, at, 0.f, P.sc, seg);
   double base[NSEG];
   return tile_scan(seg, base, sm);
 }
 
-// Block-wide OR and MIN through LDS.
-__device__ __forceinline__ void block_or_min(int &o, int &m, Smem &sm) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  o = wave_or(o);
-  m = wave_min_i(m);
-  if (lane == 0) { sm.i[0][wid] = o; sm.i[1][wid] = m; }
-  __syncthreads();
-  o = sm.i[0][0];
-  m = sm.i[1][0];
-  for (int w = 1; w < NWAVE; ++w) { o |= sm.i[0][w]; m = sm.i[1][w] < m ? sm.i[1][w] : m; }
-  __syncthreads();
-}
-
-// Sampling-mode sequence assembly (run by the last group of the sequence).
 template <int DT>
-__device__ void finish_sampling(const Params &P, int b, Smem &sm) {
-  const int tid = threadIdx.x;
-  const int k = P.k, K1 = k + 1, nT = P.nT;
-  int st = 0, j = k;
-  for (int i = tid; i <= k; i += TPB) {
-    const GroupRec r = ld_rec(P.grec + (int64_t)b * K1 + i);
-    st |= r.flags;
-    if (i < k && !r.accept && i < j) j = i;
-  }
-  for (int i = tid; i < k + 2; i += TPB) {
-    const float u = P.uniforms[(int64_t)b * (k + 2) + i];
-    if (!(u >= 0.f && u < 1.f)) st |= SV_STATUS_BAD_UNIFORM;
-  }
-  if (tid == 0 && ld_dev(P.fault)) st |= SV_STATUS_SYNC_TIMEOUT;
-  block_or_min(st, j, sm);
-  int token = -1;
-  if (!st) {
-    const int g = b * K1 + j;
-    const bool resid = j < k;
-    const GroupRec gr = ld_rec(P.grec + g);
-    for (int c = tid; c < nT; c += TPB) sm.tot[c] = ld_dev(P.rsum + (int64_t)g * nT + c);
-    __syncthreads();
-    const double u = (double)P.uniforms[(int64_t)b * (k + 2) + (resid ? k : k + 1)];
-    const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
-    const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
-    bool use_p = false;
-    for (int attempt = 0; attempt < 2; ++attempt) {
-      if (tid == 0) {
-        double R = 0.0;
-        for (int c = 0; c < nT; ++c) R += sm.tot[c];
-        const double tau = u * R;
-        double Pc = 0.0;
-        int cs = -1;
-        for (int c = 0; c < nT; ++c) {
-          const double nx = Pc + sm.tot[c];
-          if (nx > tau) { cs = c; break; }
-          Pc = nx;
-        }
-        sm.bc[2] = cs;
-        sm.dbc[0] = Pc;
-        sm.dbc[1] = tau;
-      }
-      __syncthreads();
-      if (sm.bc[2] >= 0 || attempt == 1) break;
-      // no residual mass left (rounding): draw from p_j with the same uniform
-      use_p = true;
-      for (int c = 0; c < nT; ++c) {
-        const double m = tile_mass_p<DT>(P, trow, c, gr.m_t, gr.s_t, sm);
-        if (tid == 0) sm.tot[c] = m;
-      }
-      __syncthreads();
-    }
-    const int cstar = sm.bc[2] >= 0 ? sm.bc[2] : nT - 1;
-    const double prefix = sm.dbc[0], tau = sm.dbc[1];
-    __syncthreads();
-    token = tile_draw<DT>(P, trow, drow, cstar, resid && !use_p, gr.m_t, gr.s_t, gr.m_d, gr.s_d, prefix, tau, sm);
-  }
-  if (tid == 0) {
-    if (P.status) P.status[b] = st;
-    P.accepted_len[b] = st ? -1 : j;
-  }
-  for (int i = tid; i < K1; i += TPB) {
-    int v = -1;
-    if (!st) v = i < j ? P.tokens[(int64_t)b * k + i] : (i == j ? token : -1);
-    P.out_tokens[(int64_t)b * K1 + i] = v;
-  }
-}
-
-// Greedy-mode sequence assembly: argmax-prefix match on the rows' top-1 entries.
-__device__ void finish_greedy(const Params &P, int b, Smem &sm) {
-  const int tid = threadIdx.x;
-  const int k = P.k, K1 = k + 1;
-  int st = 0, j = k;
-  for (int i = tid; i <= k; i += TPB) {
-    const int64_t g = (int64_t)b * K1 + i;
-    st |= ld_dev(&P.grec[g].flags);
-    if (i < k) {
-      const int32_t x = P.tokens[(int64_t)b * k + i];
-      if (x < 0 || x >= P.V) st |= SV_STATUS_BAD_TOKEN;
-      else if (x != ld_dev(&P.grec[g].argmax) && i < j) j = i;
-    }
-  }
-  if (tid == 0 && ld_dev(P.fault)) st |= SV_STATUS_SYNC_TIMEOUT;
-  block_or_min(st, j, sm);
-  const int aj = st ? -1 : ld_dev(&P.grec[(int64_t)b * K1 + j].argmax);
-  if (tid == 0) {
-    if (P.status) P.status[b] = st;
-    P.accepted_len[b] = st ? -1 : j;
-  }
-  for (int i = tid; i < K1; i += TPB) {
-    int v = -1;
-    if (!st) v = i < j ? P.tokens[(int64_t)b * k + i] : (i == j ? aj : -1);
-    P.out_tokens[(int64_t)b * K1 + i] = v;
-  }
-}
-
-// Sequence arrival of a group; the last group of the sequence assembles it and
-// clears the sequence's records.
-template <int DT, bool GREEDY>
-__device__ void sequence_arrival(const Params &P, int b, Smem &sm) {
-  const int tid = threadIdx.x;
-  const int K1 = P.k + 1, nT = P.nT;
-  stores_done();
-  __syncthreads();
-  if (tid == 0) sm.bc[5] = add_dev(P.seqctr + b, 1);
-  __syncthreads();
-  if (sm.bc[5] != K1 - 1) return;
-  if (GREEDY) finish_greedy(P, b, sm);
-  else finish_sampling<DT>(P, b, sm);
-  __syncthreads();
-  zero_recs(P.grec + (int64_t)b * K1, K1);
-  if (!GREEDY)
-    for (int a = tid; a < K1 * nT; a += TPB) st_dev(P.rsum + (int64_t)b * K1 * nT + a, 0.0);
-  for (int a = tid; a < K1; a += TPB) st_dev(&P.sync[(int64_t)b * K1 + a].dec, 0);
-  if (tid == 0) st_dev(P.seqctr + b, 0);
-  __syncthreads();
-}
-
-template <int DT, bool GREEDY>
-__device__ __forceinline__ void process_item(const Params &P, int item, u32x4 (&nt)[NSEG], u32x4 (&nd)[NSEG],
-                                             Smem &sm) {
-  constexpr int W = Fmt<DT>::W, TILE = Fmt<DT>::TILE;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nT = P.nT, k = P.k, K1 = k + 1, V = P.V;
-  const Geo G = geo<DT, GREEDY>(P, item);
-  const int g = G.g, c = G.c, b = G.b, i = G.i;
-  const bool pair = G.pair;
-
-  // drafted token and its two logits: every workgroup of the group decides
-  int32_t x = -1;
-  float tx = 0.f, dx = 0.f;
-  if (pair && tid == 0) {
-    x = P.tokens[(int64_t)b * k + i];
-    if (x >= 0 && x < V) { tx = load_elem<DT>(G.trow, x); dx = load_elem<DT>(G.drow, x); }
-  }
-  stage(sm, nt, nd, pair);
-
-  // ---------------- phase A: per-thread and per-tile statistics
-  const float mt = thread_max<DT>(sm, 0);
-  const float md = pair ? thread_max<DT>(sm, 1) : NEG_INF;
-  int ft = 0, fd = 0;
-  float st = 0.f, sd = 0.f;
-  if (!GREEDY) {
-    st = thread_expsum<DT>(sm, 0, mt, P.sc, ft);
-    if (pair) sd = thread_expsum<DT>(sm, 1, md, P.sc, fd);
-  } else {
-    ft = thread_has_nan<DT>(sm, 0) ? SV_STATUS_NAN : 0;
-  }
-  const bool has_elem = (int64_t)c * TILE + (int64_t)tid * W < V;
-  const uint32_t tkey = has_elem ? ordered_key(mt) : 0u;
-  {
-    const float wm_t = wave_max(mt), wm_d = wave_max(md);
-    const uint32_t wk = wave_max_u(tkey);
-    const int wf_t = wave_or(ft), wf_d = wave_or(fd);
-    if (lane == 0) { sm.f[0][wid] = wm_t; sm.f[1][wid] = wm_d; sm.u[0][wid] = wk; sm.i[0][wid] = wf_t; sm.i[1][wid] = wf_d; }
-  }
-  __syncthreads();
-  float m_ct = sm.f[0][0], m_cd = sm.f[1][0];
-  int f_ct = sm.i[0][0], f_cd = sm.i[1][0];
-  for (int w = 1; w < NWAVE; ++w) {
-    m_ct = fmaxf(m_ct, sm.f[0][w]); m_cd = fmaxf(m_cd, sm.f[1][w]);
-    f_ct |= sm.i[0][w]; f_cd |= sm.i[1][w];
-  }
-  double s_ct = 0.0, s_cd = 0.0;
-  if (!GREEDY) {
-    double a = (mt == NEG_INF) ? 0.0 : (double)st * (double)__builtin_amdgcn_exp2f((mt - m_ct) * P.sc);
-    double d = 0.0;
-    if (pair) d = (md == NEG_INF) ? 0.0 : (double)sd * (double)__builtin_amdgcn_exp2f((md - m_cd) * P.sc);
-    a = wave_sum(a);
-    d = wave_sum(d);
-    if (lane == 0) { sm.d[0][wid] = a; sm.d[1][wid] = d; }
-    __syncthreads();
-    for (int w = 0; w < NWAVE; ++w) { s_ct += sm.d[0][w]; s_cd += sm.d[1][w]; }
-  }
-
-  // ---------------- publish the tile record; start the next item's loads;
-  // wait for the whole group
-  if (tid == 0) {
-    TileRec r;
-    r.m_t = m_ct; r.m_d = m_cd; r.s_t = s_ct; r.s_d = s_cd;
-    for (int w = 0; w < NWAVE; ++w) r.wkey[w] = sm.u[0][w];
-    r.flags_t = f_ct; r.flags_d = f_cd;
-    st_rec(P.recs + item, r);
-    stores_done();
-    const int old1 = add_dev(&P.sync[g].arrive1, 1);
-    if (old1 < 0 || old1 >= nT) atomicOr(P.fault, 2);      // workspace was not zero-filled
-  }
-  if (item + (int)gridDim.x < P.items) fetch<DT, GREEDY>(P, item + gridDim.x, nt, nd);
-  if (tid == 0) wait_at_least(&P.sync[g].arrive1, nT, P.fault);
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-
-  // ---------------- phase B: row statistics, identical in every workgroup
-  // nT <= TPB: thread cc holds the record of tile cc
-  TileRec rec;
-  const bool own = tid < nT;
-  if (own) {
-    rec = ld_rec(P.recs + (int64_t)g * nT + tid);
-    for (int w = 0; w < NWAVE; ++w) sm.wkeys[tid * NWAVE + w] = rec.wkey[w];
-  } else {
-    rec.m_t = NEG_INF; rec.m_d = NEG_INF; rec.s_t = 0.0; rec.s_d = 0.0; rec.flags_t = 0; rec.flags_d = 0;
-  }
-  {
-    const float a = wave_max(rec.m_t), d = wave_max(rec.m_d);
-    const int fa = wave_or(rec.flags_t), fb = wave_or(rec.flags_d);
-    if (lane == 0) { sm.f[2][wid] = a; sm.f[3][wid] = d; sm.i[2][wid] = fa; sm.i[3][wid] = fb; }
-  }
-  __syncthreads();
-  float m_rt = sm.f[2][0], m_rd = sm.f[3][0];
-  int f_rt = sm.i[2][0], f_rd = sm.i[3][0];
-  for (int w = 1; w < NWAVE; ++w) {
-    m_rt = fmaxf(m_rt, sm.f[2][w]); m_rd = fmaxf(m_rd, sm.f[3][w]);
-    f_rt |= sm.i[2][w]; f_rd |= sm.i[3][w];
-  }
-  if (!GREEDY) {
-    double a = 0.0, d = 0.0;
-    if (own && rec.m_t != NEG_INF) a = rec.s_t * (double)__builtin_amdgcn_exp2f((rec.m_t - m_rt) * P.sc);
-    if (own && pair && rec.m_d != NEG_INF) d = rec.s_d * (double)__builtin_amdgcn_exp2f((rec.m_d - m_rd) * P.sc);
-    a = wave_sum(a);
-    d = wave_sum(d);
-    if (lane == 0) { sm.d[2][wid] = a; sm.d[3][wid] = d; }
-  }
-  // row bound for top-32 candidates: the 32nd largest wave maximum (0 when
-  // fewer than 32 waves hold elements: every element is then a candidate)
-  if (wid == 0) {
-    const int nkeys = nT * NWAVE;
-    uint32_t prefix = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = prefix | (1u << bit);
-      int cnt = 0;
-      for (int j0 = 0; j0 < nkeys; j0 += 64) {
-        const int j = j0 + lane;
-        cnt += __popcll(__ballot(j < nkeys && sm.wkeys[j] >= cand));
-      }
-      if (cnt >= TOPK) prefix = cand;
-    }
-    if (lane == 0) sm.u[1][0] = prefix;
-  }
-  __syncthreads();
-  double s_rt = 0.0, s_rd = 0.0;
-  if (!GREEDY) for (int w = 0; w < NWAVE; ++w) { s_rt += sm.d[2][w]; s_rd += sm.d[3][w]; }
-  const uint32_t L = sm.u[1][0];
-  // one data-error bit per row: NaN before +inf before an empty row
-  f_rt = (f_rt & SV_STATUS_NAN) ? SV_STATUS_NAN : f_rt;
-  f_rd = (f_rd & SV_STATUS_NAN) ? SV_STATUS_NAN : f_rd;
-  if (!GREEDY && m_rt == NEG_INF && !f_rt) f_rt = SV_STATUS_EMPTY_ROW;
-  if (pair && m_rd == NEG_INF && !f_rd) f_rd = SV_STATUS_EMPTY_ROW;
-
-  // acceptance decision of the row (one thread; tile 0 publishes it)
-  if (tid == 0) {
-    int fl = GREEDY ? (f_rt & SV_STATUS_NAN) : (f_rt | (pair ? f_rd : 0));
-    int acc = 1;
-    float pt = __builtin_nanf(""), qt = __builtin_nanf("");
-    if (pair) {
-      if (x < 0 || x >= V) {
-        fl |= SV_STATUS_BAD_TOKEN;
-        acc = 0;
-      } else if (!fl) {
-        const double p = exp2(((double)tx - (double)m_rt) * P.scd) / s_rt;
-        const double q = exp2(((double)dx - (double)m_rd) * P.scd) / s_rd;
-        const double ratio = q > 0.0 ? p / q : (p > 0.0 ? __builtin_inf() : 0.0);
-        const double a = ratio < 1.0 ? ratio : 1.0;
-        const double u = (double)P.uniforms[(int64_t)b * (k + 2) + i];
-        acc = (u < a) ? 1 : 0;
-        pt = (float)p;
-        qt = (float)q;
-      } else {
-        acc = 0;
-      }
-    }
-    sm.bc[0] = fl;
-    sm.bc[1] = acc;
-    if (c == 0) {
-      GroupRec gr;
-      gr.s_t = s_rt; gr.s_d = s_rd; gr.m_t = m_rt; gr.m_d = m_rd;
-      gr.flags = fl; gr.accept = acc; gr.argmax = -1; gr.pad = 0;
-      st_rec(P.grec + g, gr);
-      if (!GREEDY) {
-        st_dev(&P.sync[g].dec, (fl || !acc) ? 2 : 1);
-        if (P.lse_t) P.lse_t[(int64_t)b * K1 + i] = (float)((double)m_rt / (double)P.T + log(s_rt));
-        if (pair) {
-          if (P.p_tok) P.p_tok[(int64_t)b * k + i] = pt;
-          if (P.q_tok) P.q_tok[(int64_t)b * k + i] = qt;
-          if (P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)m_rd / (double)P.T + log(s_rd));
-        }
-      }
-    }
-  }
-
-  // top-32 candidates of the target row: elements at or above the bound go to
-  // this tile's slots in element order
-  {
-    const float Lf = key_value(L);
-    const int lim = V - c * TILE;                        // tile positions < lim exist
-    uint32_t mask = 0;
-    if (has_elem && (L == 0u || mt >= Lf)) {
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s) {
-        const u32x4 v = sm.tile[0][s][tid];
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          const float xv = unpack<DT>(v, w);
-          if (tpos<DT>(s, w) < lim && (L == 0u || xv >= Lf)) mask |= 1u << (s * W + w);
-        }
-      }
-    }
-    const int cnt = __popc(mask);
-    const int inc = wave_incl_int(cnt, lane);
-    if (lane == 63) sm.i[0][wid] = inc;
-    __syncthreads();
-    int slot = inc - cnt, total = 0;
-    for (int w = 0; w < NWAVE; ++w) { if (w < wid) slot += sm.i[0][w]; total += sm.i[0][w]; }
-    uint64_t *dst = P.cand + ((int64_t)g * nT + c) * SLOTS;
-    while (mask) {
-      const int bit = __builtin_ctz(mask);
-      mask &= mask - 1;
-      const int s = bit / W, w = bit - s * W;
-      const float xv = unpack<DT>(sm.tile[0][s][tid], w);
-      if (slot < SLOTS) st_dev(dst + slot, cand_key(xv, c * TILE + tpos<DT>(s, w)));
-      ++slot;
-    }
-    if (tid == 0) sm.bc[3] = total > SLOTS ? 1 : 0;
-  }
-  __syncthreads();
-  const int overflow = sm.bc[3];
-
-  // the row whose token is drawn (first rejection, or the bonus row after k
-  // acceptances) publishes its tiles' masses for the inverse-CDF draw
-  if (!GREEDY) {
-    if (tid == 0) {
-      int need = 0;
-      if (!sm.bc[0] && !(pair && sm.bc[1])) {
-        need = 1;
-        for (int l = 0; l < i; ++l) {
-          const int32_t *dp = &P.sync[(int64_t)b * K1 + l].dec;
-          wait_at_least(dp, 1, P.fault);
-          if (ld_dev(dp) != 1) { need = 0; break; }
-        }
-      }
-      sm.bc[2] = need;
-    }
-    __syncthreads();
-    if (sm.bc[2]) {
-      const float at = prob_scale(mt, m_rt, s_rt, P.sc);
-      const float ad = pair ? prob_scale(md, m_rd, s_rd, P.sc) : 0.f;
-      float seg[NSEG];
-      seg_masses<DT>(sm, pair, mt, md, at, ad, P.sc, seg);
-      double base[NSEG];
-      const double tot = tile_scan(seg, base, sm);
-      if (tid == 0) st_dev(P.rsum + item, tot);
-    }
-  }
-
-  // ---------------- group arrival; the last workgroup finishes the group
-  stores_done();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = add_dev(&P.sync[g].arrive2, (1 << 16) | overflow);
-    sm.bc[4] = ((old >> 16) == nT - 1) ? 1 + ((old & 0xffff) + overflow > 0 ? 1 : 0) : 0;
-  }
-  __syncthreads();
-  const int last = sm.bc[4];
-  if (!last) return;
-  const bool any_overflow = last == 2;
-
-  if (!GREEDY) sequence_arrival<DT, GREEDY>(P, b, sm);
-  merge_top32<DT>(P, g, b * K1 + i, any_overflow, (f_rt & SV_STATUS_NAN) != 0, G.trow, sm);
-  if (GREEDY && tid == 0) st_dev(&P.grec[g].argmax, sm.bc[7]);
-  // every workgroup of the group is past both barriers: clear the group's
-  // records and counters so the call leaves the workspace zero-filled
-  zero_recs(P.recs + (int64_t)g * nT, nT);
-  if (tid == 0) {
-    st_dev(&P.sync[g].arrive1, 0);
-    st_dev(&P.sync[g].arrive2, 0);
-  }
-  if (GREEDY) sequence_arrival<DT, GREEDY>(P, b, sm);
-}
-
-template <int DT, bool GREEDY>
-__global__ __launch_bounds__(TPB) void spec_verify_kernel(Params P) {
+__global__ __launch_bounds__(TPB) void sv_draw(Params P) {
   __shared__ Smem sm;
-  int item = blockIdx.x;
-  if (item >= P.items) return;
-  u32x4 nt[NSEG], nd[NSEG];            // the tiles of the item about to be processed
-  fetch<DT, GREEDY>(P, item, nt, nd);
-  for (; item < P.items; item += gridDim.x) {
-    process_item<DT, GREEDY>(P, item, nt, nd, sm);
-    stores_done();
+  const int tid = threadIdx.x;
+  const int nT = P.nT, k = P.k, K1 = k + 1;
+  const int b = blockIdx.x / nT, c = blockIdx.x - (blockIdx.x / nT) * nT;
+  const SeqRec sr = P.srec[b];
+  if (!sr.valid) return;
+  const int j = sr.j;
+  const bool resid = sr.resid != 0;
+  const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
+  const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
+  {
+    u32x4 rt[NSEG], rd[NSEG];
+    load_tile<DT>(trow, c, P.V, P.t_vec, rt);
+    if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
+    else
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
+    const float mt = thread_max<DT>(rt);
+    const float md = resid ? thread_max<DT>(rd) : NEG_INF;
+    const float at = prob_scale(mt, sr.m_t, sr.s_t, P.sc);
+    const float ad = resid ? prob_scale(md, sr.m_d, sr.s_d, P.sc) : 0.f;
+    float seg[NSEG];
+    seg_masses<DT>(rt, rd, resid, mt, md, at, ad, P.sc, seg);
+    double base[NSEG];
+    const double tot = tile_scan(seg, base, sm);
+    if (tid == 0) st_dev(P.rsum + (int64_t)b * nT + c, tot);
+  }
+  const int old = arrive(P.darrive + b, sm);
+  if (old < 0 || old >= nT) { if (tid == 0) atomicOr(P.fault, 2); return; }
+  if (old != nT - 1) return;
+
+  // last tile of the row: locate the crossing tile in tile order, rescan it
+  for (int cc = tid; cc < nT; cc += TPB) sm.tot[cc] = ld_dev(P.rsum + (int64_t)b * nT + cc);
+  __syncthreads();
+  bool use_p = false;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (tid == 0) {
+      double R = 0.0;
+      for (int cc = 0; cc < nT; ++cc) R += sm.tot[cc];
+      const double tau = sr.u * R;
+      double Pc = 0.0;
+      int cs = -1;
+      for (int cc = 0; cc < nT; ++cc) {
+        const double nx = Pc + sm.tot[cc];
+        if (nx > tau) { cs = cc; break; }
+        Pc = nx;
+      }
+      sm.bc[2] = cs;
+      sm.dbc[0] = Pc;
+      sm.dbc[1] = tau;
+    }
+    __syncthreads();
+    if (sm.bc[2] >= 0 || attempt == 1) break;
+    // no residual mass left (only through rounding): draw from p_j with the same uniform
+    use_p = true;
+    for (int cc = 0; cc < nT; ++cc) {
+      const double m = tile_mass_p<DT>(P, trow, cc, sr.m_t, sr.s_t, sm);
+      if (tid == 0) sm.tot[cc] = m;
+    }
     __syncthreads();
   }
+  const int cstar = sm.bc[2] >= 0 ? sm.bc[2] : nT - 1;
+  const double prefix = sm.dbc[0], tau = sm.dbc[1];
+  __syncthreads();
+  const int token = tile_draw<DT>(P, trow, drow, cstar, resid && !use_p, sr.m_t, sr.s_t, sr.m_d, sr.s_d, prefix,
+                                  tau, sm);
+  if (tid == 0) {
+    P.out_tokens[(int64_t)b * K1 + j] = token;
+    st_dev(P.darrive + b, 0);
+    SeqRec z;
+    memset(&z, 0, sizeof z);
+    P.srec[b] = z;
+  }
+  for (int cc = tid; cc < nT; cc += TPB) st_dev(P.rsum + (int64_t)b * nT + cc, 0.0);
 }
 
 // ---------------------------------------------------------------- host side
 struct Layout {
-  size_t fault, sync, seqctr, recs, rsum, grec, cand, total;
+  size_t fault, garrive, sarrive, darrive, recs, grec, srec, cand, rsum, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1055,13 +1038,15 @@ Layout layout_for(int B, int k, int V, int dtype) {
   const size_t nT = ((size_t)V + tile_of(dtype) - 1) / tile_of(dtype);
   Layout L;
   size_t o = 0;
-  L.fault = o;  o = align256(o + sizeof(int32_t));      // fixed header, same offset for every shape
-  L.sync = o;   o = align256(o + groups * sizeof(GroupSync));
-  L.seqctr = o; o = align256(o + (size_t)B * sizeof(int32_t));
-  L.recs = o;   o = align256(o + groups * nT * sizeof(TileRec));
-  L.rsum = o;   o = align256(o + groups * nT * sizeof(double));
-  L.grec = o;   o = align256(o + groups * sizeof(GroupRec));
-  L.cand = o;   o = align256(o + groups * nT * SLOTS * sizeof(uint64_t));
+  L.fault = o;   o = align256(o + sizeof(int32_t));     // fixed header, same offset for every shape
+  L.garrive = o; o = align256(o + groups * sizeof(int32_t));
+  L.sarrive = o; o = align256(o + (size_t)B * sizeof(int32_t));
+  L.darrive = o; o = align256(o + (size_t)B * sizeof(int32_t));
+  L.recs = o;    o = align256(o + groups * nT * sizeof(TileRec));
+  L.grec = o;    o = align256(o + groups * sizeof(GroupRec));
+  L.srec = o;    o = align256(o + (size_t)B * sizeof(SeqRec));
+  L.cand = o;    o = align256(o + groups * nT * SLOTS * sizeof(uint64_t));
+  L.rsum = o;    o = align256(o + (size_t)B * nT * sizeof(double));
   L.total = o;
   return L;
 }
@@ -1071,39 +1056,17 @@ bool shape_ok(const sv_shape_t *s) {
          (int64_t)s->V <= (int64_t)MAX_TILES * tile_of(s->dtype);
 }
 
-struct DeviceInfo {
-  bool ready = false;
-  int cus = 0, coop = 0;
-  int occ[4] = {0, 0, 0, 0};
-};
-std::mutex g_mu;
-DeviceInfo g_dev[64];
-
-typedef void (*kernel_fn)(Params);
-kernel_fn kernel_for(int dtype, bool greedy) {
-  if (dtype == SV_BF16) return greedy ? spec_verify_kernel<SV_BF16, true> : spec_verify_kernel<SV_BF16, false>;
-  return greedy ? spec_verify_kernel<SV_F32, true> : spec_verify_kernel<SV_F32, false>;
-}
-
-int device_info(DeviceInfo *&out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SV_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceInfo &d = g_dev[dev];
-  if (!d.ready) {
-    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return SV_ERR_HIP;
-    if (hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) return SV_ERR_HIP;
-    for (int v = 0; v < 4; ++v) {
-      int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void *)kernel_for(v >> 1, v & 1), TPB, 0) !=
-          hipSuccess)
-        return SV_ERR_HIP;
-      d.occ[v] = nb;
-    }
-    d.ready = true;
+template <int DT> hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
+  const unsigned items = (unsigned)((int64_t)P.B * (P.k + 1) * P.nT);
+  if (greedy) {
+    hipLaunchKernelGGL((sv_stream<DT, true>), dim3(items), dim3(TPB), 0, stream, P);
+    return hipGetLastError();
   }
-  out = &d;
-  return SV_OK;
+  hipLaunchKernelGGL((sv_stream<DT, false>), dim3(items), dim3(TPB), 0, stream, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sv_draw<DT>), dim3((unsigned)((int64_t)P.B * P.nT)), dim3(TPB), 0, stream, P);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1124,7 +1087,7 @@ extern "C" const char *spec_verify_error_string(int code) {
     case SV_ERR_DTYPE: return "dtype must be SV_F32 or SV_BF16";
     case SV_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than spec_verify_workspace_bytes";
     case SV_ERR_HIP: return "HIP runtime call or kernel launch failed";
-    case SV_ERR_DEVICE: return "current device does not support cooperative launch";
+    case SV_ERR_DEVICE: return "current device is not usable";
     default: return "unknown error code";
   }
 }
@@ -1153,11 +1116,6 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   const Layout L = layout_for(s.B, s.k, s.V, s.dtype);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return SV_ERR_WORKSPACE;
 
-  DeviceInfo *dev = nullptr;
-  int rc = device_info(dev);
-  if (rc != SV_OK) return rc;
-  if (!dev->coop) return SV_ERR_DEVICE;
-
   char *ws = (char *)workspace;
   Params P;
   const int esz = s.dtype == SV_BF16 ? 2 : 4;
@@ -1176,41 +1134,26 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   P.lse_d = aux ? aux->lse_draft : nullptr;
   P.p_tok = aux ? aux->p_tok : nullptr;
   P.q_tok = aux ? aux->q_tok : nullptr;
-  P.sync = (GroupSync *)(ws + L.sync);
-  P.seqctr = (int32_t *)(ws + L.seqctr);
   P.fault = (int32_t *)(ws + L.fault);
+  P.garrive = (int32_t *)(ws + L.garrive);
+  P.sarrive = (int32_t *)(ws + L.sarrive);
+  P.darrive = (int32_t *)(ws + L.darrive);
   P.recs = (TileRec *)(ws + L.recs);
-  P.rsum = (double *)(ws + L.rsum);
   P.grec = (GroupRec *)(ws + L.grec);
+  P.srec = (SeqRec *)(ws + L.srec);
   P.cand = (uint64_t *)(ws + L.cand);
+  P.rsum = (double *)(ws + L.rsum);
   P.B = s.B;
   P.k = s.k;
   P.V = s.V;
   P.nT = (int32_t)nT;
-  P.items = (int32_t)items;
   P.T = greedy ? 0.f : s.temperature;
   P.scd = greedy ? 0.0 : 1.4426950408889634 / (double)s.temperature;
   P.sc = (float)P.scd;
   P.t_vec = (((uintptr_t)target_logits & 15) == 0 && ((ts * esz) & 15) == 0) ? 1 : 0;
   P.d_vec = (!greedy && s.k > 0 && ((uintptr_t)draft_logits & 15) == 0 && ((ds * esz) & 15) == 0) ? 1 : 0;
 
-  const int variant = (s.dtype == SV_BF16 ? 2 : 0) + (greedy ? 1 : 0);
-  const int64_t resident = (int64_t)dev->occ[variant] * dev->cus;
-  int64_t grid = resident;
-  if (const char *lim = getenv("SV_GRID_LIMIT")) {
-    const long v = strtol(lim, nullptr, 10);
-    if (v > 0 && v < grid) grid = v;
-  }
-  if (grid < nT) grid = nT;                      // a group must fit on the device at once
-  if (grid > resident) return SV_ERR_DEVICE;
-  if (grid > items) grid = items;
-
-  void *args[] = {&P};
-  hipError_t e = hipLaunchCooperativeKernel((const void *)kernel_for(s.dtype, greedy), dim3((unsigned)grid),
-                                            dim3(TPB), args, 0, (hipStream_t)stream);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return SV_ERR_HIP;
-  }
-  return SV_OK;
+  const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, (hipStream_t)stream)
+                                          : launch<SV_F32>(P, greedy, (hipStream_t)stream);
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
