@@ -161,7 +161,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "spec_verify_kernel", "kernel_us_mean": round(kern_avg * 1e3, 3),
+                     "kernel": "sv_verify", "kernel_us_mean": round(kern_avg * 1e3, 3),
                      "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, q)) * 1e3, 3) for q in (10, 50, 90)]},
         "mean_accepted_len": float(np.mean(g["accepted_len"])),
         "mean_accepted_len_plus1": float(np.mean(g["accepted_len"]) + 1),

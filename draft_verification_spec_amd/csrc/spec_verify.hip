@@ -1,40 +1,46 @@
 // spec_verify.hip -- speculative-sampling verification for gfx950 (MI355X).
 //
-// Two plain launches; no workgroup ever waits for another.
+// Two launches.
 //
-//  sv_stream  one workgroup per (group, tile).  A group is, for i < k, the pair
+//  sv_verify  one workgroup per (group, tile).  A group is, for i < k, the pair
 //             (target row i, draft row i) of a sequence and, for i == k, target
 //             row k alone; in greedy mode every group is one target row.  Tiles
-//             are fixed vocabulary slices (4096 bf16 or 2048 fp32 entries, 8 KB
-//             of each row).  Each workgroup streams its tile(s) once with 128-bit
-//             loads and publishes a tile record:
+//             are fixed 16 KB slices of a row (8192 bf16 or 4096 fp32 entries).
+//             Each workgroup streams its tile(s) once with 128-bit loads and
+//             publishes a tile record:
 //               - max and sum of exp2((x - max) * log2(e)/T) of each row part
-//                 (fp32 exp, per-thread fp32 sums, fp64 above the thread);
-//               - the tile's 8 largest lane maxima (a lane owns 16 elements of
-//                 a bf16 tile, 8 of an fp32 tile);
-//             and, as top-32 candidates, the elements at or above the 8th of
-//             those lane maxima.
-//             The last workgroup of a group to publish combines the records in
-//             tile order, takes the acceptance decision and merges the top-32.
-//             The 32nd largest of all the tiles' lane maxima is a lower bound of
-//             the row's 32nd largest element (32 distinct elements reach it).
-//             Candidates at or above it are ranked; a tile whose 8th lane
-//             maximum lies above the bound may hold further elements above it
-//             and is rescanned, as is a tile whose candidates overflowed.
-//             The last group of a sequence finds the first rejection j (greedy:
-//             the first draft that differs from the argmax).
-//  sv_draw    sampling only.  After a rejection at j every tile of pair row j
-//             publishes its residual mass max(0, p - q); the last one draws by
-//             inverse CDF over the tile masses in tile order and rescans the
-//             crossing tile.  After k acceptances a single workgroup draws from
-//             p_k, whose tile masses the merge of row k has already published.
+//                 (fp32 exp and per-thread fp32 sums, fp64 above the thread);
+//               - 8 of the tile's largest lane maxima (a lane owns 32 bf16 or
+//                 16 fp32 elements);
+//             and, as top-32 candidates, the elements at or above the 16-bit
+//             key bucket of the 8th largest lane maximum.
+//             The last tile of a group (dispatched after the others) waits for
+//             the others' records and merges the group: row max and normaliser
+//             in tile order, the acceptance decision, and the top-32.  The 32nd
+//             largest of the tiles' lane maxima bounds the row's 32nd largest
+//             element from below; candidates at or above it are ranked, and a
+//             tile whose candidate threshold lies above the bound (it may hold
+//             further elements above it) is rescanned, as is a tile whose
+//             candidates overflowed their slots.  The merge of row k also
+//             publishes the tile masses of p_k.
+//             The merge of row k (dispatched after rows 0..k-1) waits for the
+//             sequence's other groups and assembles it: the first rejection j
+//             (greedy: the first draft that differs from the argmax) and the
+//             tokens, except the one to draw.
+//  sv_draw    sampling only, one workgroup per (sequence, tile).  After a
+//             rejection at j every tile of pair row j publishes its residual
+//             mass max(0, p - q); the last one draws by inverse CDF over the tile
+//             masses in tile order and rescans the crossing tile.  After k
+//             acceptances one workgroup draws from p_k over the published masses.
 //
-// Wave-level reductions and scans run on DPP row shifts and broadcasts in a
-// fixed order, so every reduction is deterministic.  Cross-workgroup data within
-// a launch moves through the workspace with device-scope write-through stores
-// and device-scope loads, ordered by waiting for the stores to complete before
-// the counter that announces them is bumped.  No workgroup waits for another,
-// so any dispatch order and any occupancy are safe.
+// In sv_verify, waiting only ever happens on workgroups with a lower index,
+// which the hardware dispatches first, and every wait is bounded in time: a wait that
+// gives up sets the fault word (reported as SV_STATUS_SYNC_TIMEOUT) and the
+// kernel still finishes.  Data moves between workgroups through the workspace
+// with device-scope write-through stores and device-scope loads, ordered by
+// waiting for the stores to complete before the counter or flag that announces
+// them is written.  Wave-level reductions and scans run on DPP row shifts and
+// broadcasts in a fixed order, so every reduction is deterministic.
 //
 // Acceptance test, residual and bonus draw follow the ReSpec notes ("2 .
 // background": one-shot acceptance test Eq.1, residual max(0,p-q)/sum); the
@@ -53,42 +59,34 @@ namespace {
 
 constexpr int TPB = 256;               // threads per workgroup (4 waves of 64)
 constexpr int NWAVE = TPB / 64;
-constexpr int NSEG = 2;                // 16-byte vectors per thread per row
+constexpr int NSEG = 4;                // 16-byte vectors per thread per row
 constexpr int LIST = 8;                // lane maxima a tile record keeps
 constexpr int SLOTS = 16;              // candidate slots per tile
 constexpr int MERGE_CAP = 512;         // candidates a row merge ranks in LDS
 constexpr int TOPK = SV_TOPK;
-constexpr int MAX_TILES = 128;
+constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
-constexpr int RECW_PT = MAX_TILES * 8 / TPB;       // tile-record words per merge thread
-constexpr int TOPS_PL = MAX_TILES * LIST / 64;     // lane maxima per lane in the bound search
 constexpr float NEG_INF = -__builtin_inff();
+constexpr uint64_t SPIN_TICKS = 20000000;          // bounded waits give up after 0.2 s (100 MHz clock)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// E: bytes per element; W: elements per 16-byte vector; TILE: elements per
-// tile; LOW / BITS: ordered keys of this format leave LOW in their low bits,
-// and only the top BITS bits separate values.
+// E: bytes per element; W: elements per 16-byte vector; TILE: elements per tile
 template <int DT> struct Fmt;
-template <> struct Fmt<SV_BF16> {
-  static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8, BITS = 16;
-  static constexpr uint32_t LOW = 0xffffu;
-};
-template <> struct Fmt<SV_F32> {
-  static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4, BITS = 32;
-  static constexpr uint32_t LOW = 0u;
-};
+template <> struct Fmt<SV_BF16> { static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8; };
+template <> struct Fmt<SV_F32> { static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4; };
 
-// Published per (group, tile) by sv_stream.
+// Published per (group, tile) by the stream workgroups; 8 words.
 struct TileRec {
   float m_t, m_d;          // tile max of the target / draft row part
   double s_t, s_d;         // sum exp2((x - m) * sc) over the tile part
   int32_t flags_t, flags_d;
-  uint32_t top[LIST];      // ordered keys of the tile's largest lane maxima, descending (0: no lane)
+  uint32_t top[LIST];      // ordered keys of 8 largest lane maxima (0: no lane); top[7] lies
+                           // in the 16-bit bucket of the candidate threshold
 };
 static_assert(sizeof(TileRec) == 64, "tile record");
 
-// Published per group by its last workgroup.
+// Published per group by its merging workgroup.
 struct GroupRec {
   double s_t, s_d;         // row normalisers (relative to m_t, m_d)
   float m_t, m_d;          // row maxima
@@ -98,7 +96,7 @@ struct GroupRec {
   int32_t pad;
 };
 
-// Handed from sv_stream to sv_draw per sequence (valid == 1: a token to draw).
+// Handed from sv_verify to sv_draw per sequence (valid == 1: a token to draw).
 struct SeqRec {
   double s_t, s_d;         // normalisers of the drawing row's target / draft part
   float m_t, m_d;
@@ -114,7 +112,7 @@ struct Params {
   const float *uniforms;
   int32_t *accepted_len, *out_tokens, *topk_idx, *status;
   float *topk_val, *lse_t, *lse_d, *p_tok, *q_tok;
-  int32_t *fault;                      // set when the workspace was not zero-filled
+  int32_t *fault;                      // bit 1: a wait gave up; bit 2: workspace not zero-filled
   int32_t *garrive, *sarrive, *darrive;
   TileRec *recs;
   GroupRec *grec;
@@ -131,24 +129,22 @@ struct Params {
 
 struct Smem {
   union {
-    uint32_t w8[NWAVE * LIST];         // stream: each wave's largest lane maxima
-    struct {
-      TileRec rec[MAX_TILES];          // row merge: the group's tile records
-      uint64_t keys[MERGE_CAP];        // row merge: candidates at or above the bound
-    } m;
+    uint64_t keys[MERGE_CAP];          // row merge: candidates at or above the bound
     struct {                           // exact top-32 fallback
       uint32_t hist[2048];
       int32_t part[TPB];
       uint64_t list[TOPK];
     } fb;
-    double tot[MAX_TILES];             // draw: tile masses
   };
+  uint32_t w8[NWAVE * LIST];           // stream: each wave's largest lane maxima
+  uint32_t t8[LIST];                   // stream: the tile's list
+  double tot[MAX_TILES];               // draw: tile masses in tile order
   float f[4][NWAVE];
   int32_t i[4][NWAVE];
   double d[4][NWAVE];
   int32_t bc[8];
   double dbc[8];
-  uint64_t rescan[2];                  // row merge: tiles to rescan
+  uint64_t rescan;                     // row merge: tiles to rescan
 };
 
 // ---------------------------------------------------------------- helpers
@@ -201,7 +197,6 @@ template <class Op> __device__ __forceinline__ uint32_t wave_red(uint32_t v, uin
   v = op(v, dpp<0x143, 0xc, 0xf>(id, v));   // row_bcast:31 into rows 2, 3
   return readlane(v, 63);
 }
-struct OpMaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
 struct OpMaxI { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return (int)a > (int)b ? a : b; } };
 struct OpMinI { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return (int)a < (int)b ? a : b; } };
 struct OpOr { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
@@ -210,7 +205,6 @@ struct OpMaxF {
     return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
   }
 };
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) { return wave_red(v, 0u, OpMaxU()); }
 __device__ __forceinline__ int wave_max_i(int v) { return (int)wave_red((uint32_t)v, 0x80000000u, OpMaxI()); }
 __device__ __forceinline__ int wave_min_i(int v) { return (int)wave_red((uint32_t)v, 0x7fffffffu, OpMinI()); }
 __device__ __forceinline__ int wave_or(int v) { return (int)wave_red((uint32_t)v, 0u, OpOr()); }
@@ -241,20 +235,32 @@ __device__ __forceinline__ double wave_scan_d(double x) {
 // value of the previous lane of the wave (0 in lane 0)
 __device__ __forceinline__ double wave_prev_d(double v) { return dpp_d<0x138, 0xf, 0xf>(v); }
 
-// The LIST largest keys among the wave's lanes, descending: lane r < LIST
-// receives the r-th (0 where fewer lanes hold a nonzero key).  Equal keys of
-// different lanes count separately.
-__device__ __forceinline__ uint32_t wave_top_list(uint32_t key, int lane) {
-  uint32_t mine = 0;
+// ---- lists of largest keys.  Keys are compared on their top 16 bits (a bf16
+// value's whole key; an fp32 key's sign, exponent and 7 mantissa bits).
+// The largest K = P << 16 such that at least LIST lanes hold a key >= K (0 when
+// fewer than LIST lanes hold a nonzero key).
+__device__ __forceinline__ uint32_t list_bound(uint32_t key) {
+  uint32_t K = 0;
 #pragma unroll
-  for (int r = 0; r < LIST; ++r) {
-    const uint32_t m = wave_max_u(key);
-    const uint64_t hit = __ballot(key == m && m != 0u);
-    const int sel = hit ? __builtin_ctzll(hit) : 64;
-    if (lane == sel) key = 0u;
-    if (lane == r) mine = m;
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t c = K | (1u << bit);
+    if (__popcll(__ballot(key >= c)) >= LIST) K = c;
   }
-  return mine;
+  return K;
+}
+// This lane's position in the wave's list of LIST largest keys under bound K:
+// keys above K's bucket first, then keys in it, each in lane order; -1 if the
+// key is not listed.  *n receives the list length (<= LIST).
+__device__ __forceinline__ int list_pos(uint32_t key, uint32_t K, int lane, int *n) {
+  const bool above = key != 0u && (key >> 16) > (K >> 16);
+  const bool tie = key != 0u && (key >> 16) == (K >> 16);
+  const uint64_t ma = __ballot(above), mt = __ballot(tie);
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int a = __popcll(ma), len = a + __popcll(mt);
+  *n = len < LIST ? len : LIST;
+  if (above) return __popcll(ma & below);
+  if (tie) { const int p = a + __popcll(mt & below); return p < LIST ? p : -1; }
+  return -1;
 }
 
 // Device-scope accesses: loads see the latest device-visible value; stores are
@@ -268,6 +274,9 @@ template <class T> __device__ __forceinline__ void st_dev(T *p, T v) {
 __device__ __forceinline__ int add_dev(int32_t *p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void add_dev_noret(int32_t *p, int v) {
+  (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait until this wave's earlier memory accesses have completed (and keep the
 // compiler from moving memory accesses across the wait).
 __device__ __forceinline__ void stores_done() {
@@ -275,11 +284,31 @@ __device__ __forceinline__ void stores_done() {
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
+// All of the workgroup's stores have completed (every wave waited for its own).
+__device__ __forceinline__ void block_stores_done() {
+  stores_done();
+  __syncthreads();
+}
+// Bounded wait of one thread until *p >= target.  Returns the value seen;
+// on timeout sets fault bit 1 and returns what it last saw.
+__device__ __forceinline__ int wait_at_least(const int32_t *p, int target, int32_t *fault) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  int v = ld_dev(p);
+  while (v < target) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+      atomicOr(fault, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = ld_dev(p);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return v;
+}
 // Announce this workgroup's published data on a counter; returns the count
 // before it (the same value in every thread).
 __device__ __forceinline__ int arrive(int32_t *ctr, Smem &sm) {
-  stores_done();
-  __syncthreads();
+  block_stores_done();
   if (threadIdx.x == 0) sm.bc[7] = add_dev(ctr, 1);
   __syncthreads();
   const int old = sm.bc[7];
@@ -385,14 +414,14 @@ __device__ __forceinline__ float scaled_exp(float x, float m, float sc) {
   return __builtin_amdgcn_exp2f((x - ms) * sc);
 }
 
-// Sequential fp32 sum of the thread's scaled exps; flags NaN / +inf.
+// Sequential fp32 sum of the thread's exp2((x - ref) * sc); flags NaN / +inf.
 template <int DT>
-__device__ __forceinline__ float thread_expsum(const u32x4 (&r)[NSEG], float m, float sc, int &flags) {
+__device__ __forceinline__ float thread_expsum(const u32x4 (&r)[NSEG], float ref, float sc, int &flags) {
   float s = 0.f;
 #pragma unroll
   for (int g = 0; g < NSEG; ++g)
 #pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) s += scaled_exp(unpack<DT>(r[g], w), m, sc);
+    for (int w = 0; w < Fmt<DT>::W; ++w) s += __builtin_amdgcn_exp2f((unpack<DT>(r[g], w) - ref) * sc);
   flags = 0;
   if (!(s == s)) flags = thread_has_nan<DT>(r) ? SV_STATUS_NAN : SV_STATUS_POSINF;
   return s;
@@ -437,7 +466,7 @@ __device__ __forceinline__ void seg_masses(const u32x4 (&rt)[NSEG], const u32x4 
 // tile's element order (vector-major, then thread).  base[s] receives the mass
 // of all tile elements before this thread's vector s; returns the tile total.
 // Fixed association: identical bits wherever it is evaluated.
-__device__ double tile_scan(const float (&seg)[NSEG], double (&base)[NSEG], Smem &sm) {
+__device__ __forceinline__ double tile_scan(const float (&seg)[NSEG], double (&base)[NSEG], Smem &sm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   double prev[NSEG];
 #pragma unroll
@@ -479,7 +508,7 @@ __device__ __forceinline__ void block_or_min(int &o, int &m, Smem &sm) {
 // when more candidates reach the bound than the merge holds: heavy ties).
 // Rank 0's index goes to sm.bc[6].
 template <int DT>
-__device__ void topk_exact(const char *row, int V, float *oval, int32_t *oidx, Smem &sm) {
+__device__ __forceinline__ void topk_exact(const char *row, int V, float *oval, int32_t *oidx, Smem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int need = V < TOPK ? V : TOPK;
   uint32_t prefix = 0, pmask = 0;
@@ -564,6 +593,137 @@ __device__ void topk_exact(const char *row, int V, float *oval, int32_t *oidx, S
   __syncthreads();
 }
 
+// Inverse-CDF draw inside one tile: the first element (ascending index) of
+// positive mass whose cumulative mass prefix + (scan base + running fp32 sum)
+// exceeds tau; if rounding leaves none, the tile's last positive-mass element
+// (-1 when the tile has none).  The masses are recomputed exactly as when the
+// tile's total was published.  The running sum never decreases inside a
+// vector, so each thread recomputes only its first vector whose end exceeds
+// tau.
+template <int DT>
+__device__ __forceinline__ int tile_draw(const Params &P, const char *trow, const char *drow, int c, bool resid,
+                                         float m_t, double s_t, float m_d, double s_d, double prefix, double tau,
+                                         Smem &sm) {
+  constexpr int W = Fmt<DT>::W;
+  u32x4 rt[NSEG], rd[NSEG];
+  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
+  if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
+  else
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
+  const float mt = thread_max<DT>(rt);
+  const float md = resid ? thread_max<DT>(rd) : NEG_INF;
+  const float at = prob_scale(mt, m_t, s_t, P.sc);
+  const float ad = resid ? prob_scale(md, m_d, s_d, P.sc) : 0.f;
+  float seg[NSEG];
+  seg_masses<DT>(rt, rd, resid, mt, md, at, ad, P.sc, seg);
+  double base[NSEG];
+  tile_scan(seg, base, sm);
+  int sel = -1;
+  double bsel = 0.0;
+  u32x4 vt = rt[0], vd = rd[0];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s)
+    if (sel < 0 && prefix + (base[s] + (double)seg[s]) > tau) { sel = s; bsel = base[s]; vt = rt[s]; vd = rd[s]; }
+  int first = 0x7fffffff;
+  if (sel >= 0) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mval = elem_mass<DT>(vt, vd, w, resid, mt, md, at, ad, P.sc);
+      a += mval;
+      if (first == 0x7fffffff && mval > 0.f && prefix + (bsel + (double)a) > tau) first = tpos<DT>(sel, w);
+    }
+  }
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  first = wave_min_i(first);
+  if (lane == 0) sm.i[2][wid] = first;
+  __syncthreads();
+  int f = sm.i[2][0];
+  for (int w = 1; w < NWAVE; ++w) f = sm.i[2][w] < f ? sm.i[2][w] : f;
+  __syncthreads();
+  if (f != 0x7fffffff) return c * Fmt<DT>::TILE + f;
+  // no crossing inside the tile (rounding): its last positive-mass element,
+  // in each thread's last vector of positive mass
+  int lsel = -1;
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s)
+    if (seg[s] > 0.f) { lsel = s; vt = rt[s]; vd = rd[s]; }
+  int lastpos = -1;
+  if (lsel >= 0) {
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      if (elem_mass<DT>(vt, vd, w, resid, mt, md, at, ad, P.sc) > 0.f) lastpos = tpos<DT>(lsel, w);
+  }
+  lastpos = wave_max_i(lastpos);
+  if (lane == 0) sm.i[3][wid] = lastpos;
+  __syncthreads();
+  int l = sm.i[3][0];
+  for (int w = 1; w < NWAVE; ++w) l = sm.i[3][w] > l ? sm.i[3][w] : l;
+  __syncthreads();
+  return l < 0 ? -1 : c * Fmt<DT>::TILE + l;
+}
+
+// Total target mass p of one tile (the arithmetic of tile_draw without a draft row).
+template <int DT>
+__device__ __forceinline__ double tile_mass_p(const Params &P, const char *trow, int c, float m_t, double s_t, Smem &sm) {
+  u32x4 rt[NSEG];
+  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
+  const float mt = thread_max<DT>(rt);
+  const float at = prob_scale(mt, m_t, s_t, P.sc);
+  float seg[NSEG];
+  seg_masses<DT>(rt, rt, false, mt, NEG_INF, at, 0.f, P.sc, seg);
+  double base[NSEG];
+  return tile_scan(seg, base, sm);
+}
+
+// The crossing tile of tau = u * R over the tile masses in sm.tot (tile order,
+// R their sum): sm.bc[2] = the first tile whose cumulative mass exceeds tau (-1
+// if none), sm.dbc[0] = the mass before it, sm.dbc[1] = tau.  Run by wave 0.
+__device__ __forceinline__ void locate_tile(int nT, double u, Smem &sm) {
+  const int lane = threadIdx.x & 63;
+  const double cum = wave_scan_d(lane < nT ? sm.tot[lane] : 0.0);
+  const double tau = u * readlane_d(cum, 63);
+  const uint64_t h = __ballot(lane < nT && cum > tau);
+  const int cs = h ? __builtin_ctzll(h) : -1;
+  const double before = cs > 0 ? readlane_d(cum, cs - 1) : 0.0;
+  if (lane == 0) { sm.bc[2] = cs; sm.dbc[0] = before; sm.dbc[1] = tau; }
+}
+
+// Inverse-CDF draw of one token over sm.tot (tile masses of a row in tile
+// order): the crossing tile, then the element inside it.  A residual with no
+// mass left (only through rounding) falls back to p of the same row with the
+// same uniform.  Every thread of the workgroup calls it; returns the token.
+template <int DT>
+__device__ __forceinline__ int draw_row(const Params &P, const char *trow, const char *drow, bool resid, float m_t, double s_t,
+                        float m_d, double s_d, double u, Smem &sm) {
+  const int tid = threadIdx.x, wid = tid >> 6, nT = P.nT;
+  __syncthreads();
+  if (wid == 0) locate_tile(nT, u, sm);
+  __syncthreads();
+  bool use_p = false;
+  if (sm.bc[2] < 0 && resid) {
+    use_p = true;
+    for (int cc = 0; cc < nT; ++cc) {
+      const double m = tile_mass_p<DT>(P, trow, cc, m_t, s_t, sm);
+      if (tid == 0) sm.tot[cc] = m;
+    }
+    __syncthreads();
+    if (wid == 0) locate_tile(nT, u, sm);
+    __syncthreads();
+  }
+  const int cstar = sm.bc[2] >= 0 ? sm.bc[2] : nT - 1;
+  const double prefix = sm.dbc[0], tau = sm.dbc[1];
+  __syncthreads();
+  const bool rmode = resid && !use_p;
+  int token = tile_draw<DT>(P, trow, drow, cstar, rmode, m_t, s_t, m_d, s_d, prefix, tau, sm);
+  // a tile whose recomputed masses all rounded to zero: the last positive-mass
+  // element before it
+  for (int cc = cstar - 1; token < 0 && cc >= 0; --cc)
+    token = tile_draw<DT>(P, trow, drow, cc, rmode, m_t, s_t, m_d, s_d, 0.0, __builtin_inf(), sm);
+  return token;
+}
+
 struct Geo {
   int g, c, b, i;
   bool pair;
@@ -583,11 +743,11 @@ template <int DT, bool GREEDY> __device__ __forceinline__ Geo geo(const Params &
   return G;
 }
 
-// Sequence assembly in sv_stream (run by the last group of the sequence):
-// greedy emits everything; sampling emits all but the drawn token and hands
-// the drawing row to sv_draw.
-template <bool GREEDY>
-__device__ void seq_finish(const Params &P, int b, Smem &sm) {
+// Sequence assembly (run by the merge of row k once the sequence's other
+// groups have published): status, first rejection j, and the tokens; greedy
+// emits everything, sampling hands the drawing row to sv_draw.
+template <int DT, bool GREEDY>
+__device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
   const int tid = threadIdx.x;
   const int k = P.k, K1 = k + 1;
   const bool small = k + 2 <= TPB;           // one entry per thread: no reloads
@@ -618,62 +778,55 @@ __device__ void seq_finish(const Params &P, int b, Smem &sm) {
   }
   if (tid == 0 && ld_dev(P.fault)) st |= SV_STATUS_SYNC_TIMEOUT;
   block_or_min(st, j, sm);
-  // the drawing row's record and uniform reach thread 0 through LDS
+  // the drawing row's record and uniform reach every thread through LDS
   const int ui = j < k ? k : k + 1;
   if (small && tid == j) {
-    sm.dbc[0] = mine.s_t; sm.dbc[1] = mine.s_d;
+    sm.dbc[4] = mine.s_t; sm.dbc[5] = mine.s_d;
     sm.f[0][0] = mine.m_t; sm.f[0][1] = mine.m_d;
     sm.bc[1] = mine.argmax;
   }
-  if (small && tid == ui) sm.dbc[2] = (double)uu;
+  if (small && tid == ui) sm.dbc[6] = (double)uu;
+  if (!small && tid == 0) {
+    const GroupRec rj = ld_rec(P.grec + (int64_t)b * K1 + j);
+    sm.dbc[4] = rj.s_t; sm.dbc[5] = rj.s_d; sm.f[0][0] = rj.m_t; sm.f[0][1] = rj.m_d; sm.bc[1] = rj.argmax;
+    sm.dbc[6] = GREEDY ? 0.0 : (double)P.uniforms[(int64_t)b * (k + 2) + ui];
+  }
   __syncthreads();
+  const double s_t = sm.dbc[4], s_d = sm.dbc[5], u = sm.dbc[6];
+  const float m_t = sm.f[0][0], m_d = sm.f[0][1];
+  const int amax = sm.bc[1];
   if (tid == 0) {
     if (P.status) P.status[b] = st;
     P.accepted_len[b] = st ? -1 : j;
-    GroupRec rj;
-    double u;
-    if (small) {
-      rj.s_t = sm.dbc[0]; rj.s_d = sm.dbc[1]; rj.m_t = sm.f[0][0]; rj.m_d = sm.f[0][1]; rj.argmax = sm.bc[1];
-      u = sm.dbc[2];
-    } else {
-      rj = ld_rec(P.grec + (int64_t)b * K1 + j);
-      u = GREEDY ? 0.0 : (double)P.uniforms[(int64_t)b * (k + 2) + ui];
-    }
-    if (GREEDY) {
-      sm.bc[2] = rj.argmax;
-    } else if (!st) {
-      SeqRec sr;
-      sr.s_t = rj.s_t; sr.s_d = rj.s_d; sr.m_t = rj.m_t; sr.m_d = rj.m_d;
-      sr.j = j; sr.valid = 1;
-      sr.u = u;
-      sr.resid = j < k ? 1 : 0; sr.pad = 0;
-      P.srec[b] = sr;                  // read by sv_draw after this launch
-    }
   }
-  __syncthreads();
   for (int i = tid; i < K1; i += TPB) {
     int v = -1;
     if (!st && i < j) v = i < TPB ? tok : P.tokens[(int64_t)b * k + i];
-    if (!st && i == j && GREEDY) v = sm.bc[2];
+    if (!st && i == j && GREEDY) v = amax;
     if (st || i != j || GREEDY) P.out_tokens[(int64_t)b * K1 + i] = v;
   }
   zero_recs(P.grec + (int64_t)b * K1, K1);
-  if (tid == 0) st_dev(P.sarrive + b, 0);
+  if (!GREEDY && !st && tid == 0) {
+    SeqRec sr;
+    sr.s_t = s_t; sr.s_d = s_d; sr.m_t = m_t; sr.m_d = m_d;
+    sr.j = j; sr.valid = 1; sr.u = u;
+    sr.resid = j < k ? 1 : 0; sr.pad = 0;
+    st_rec(P.srec + b, sr);            // read by sv_draw after this launch
+  }
 }
 
-// Row combine, acceptance decision and top-32 merge of group g (run by the
-// last workgroup of the group to publish), then the sequence's arrival.
+// Row combine, acceptance decision and top-32 merge of group g (run by its last
+// tile once the others have published), then the sequence's arrival.
 template <int DT, bool GREEDY>
-__device__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm) {
-  constexpr uint32_t LOW = Fmt<DT>::LOW;
+__device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int nT = P.nT, k = P.k, K1 = k + 1, V = P.V;
   const int g = G.g, b = G.b, i = G.i;
   const bool pair = G.pair;
-  const int nslot = nT * SLOTS, nrecw = nT * 8;
+  const int nslot = nT * SLOTS;
 
-  // ---- one round of loads: candidate slots (kept in registers), tile records
-  // and overflow flags (to LDS), the drafted token's logits and its uniform
+  // ---- one round of loads: candidate slots (all threads), tile records and
+  // overflow flags (wave 0, lane t: tile t), the drafted token's logits and uniform
   uint64_t *slots = P.cand + (int64_t)g * nslot;
   uint64_t key[KEYS_PT];
 #pragma unroll
@@ -681,59 +834,33 @@ __device__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm)
     const int a = tid + q * TPB;
     key[q] = a < nslot ? ld_dev(slots + a) : 0ull;
   }
-  const uint64_t *rsrc = (const uint64_t *)(P.recs + (int64_t)g * nT);
-  uint64_t rw[RECW_PT];
+  uint64_t *rsrc = (uint64_t *)(P.recs + (int64_t)g * nT) + lane * 8;
+  uint64_t rw[8];
+  int32_t ov = 0;
+  const bool own = wid == 0 && lane < nT;
 #pragma unroll
-  for (int q = 0; q < RECW_PT; ++q) {
-    const int a = tid + q * TPB;
-    rw[q] = a < nrecw ? ld_dev(rsrc + a) : 0ull;
-  }
-  const int32_t ov = tid < nT ? ld_dev(P.ovf + (int64_t)g * nT + tid) : 0;
+  for (int q = 0; q < 8; ++q) rw[q] = own ? ld_dev(rsrc + q) : 0ull;
+  if (own) ov = ld_dev(P.ovf + (int64_t)g * nT + lane);
   float lv = 0.f;                              // lane 0: t_x, lane 1: d_x
   float ui = 0.f;
   if (pair && wid == 0 && lane < 2 && x >= 0 && x < V) lv = load_elem<DT>(lane == 0 ? G.trow : G.drow, x);
   if (pair && tid == 0) ui = P.uniforms[(int64_t)b * (k + 2) + i];
-  uint64_t *rdst = (uint64_t *)sm.m.rec;
-#pragma unroll
-  for (int q = 0; q < RECW_PT; ++q) {
-    const int a = tid + q * TPB;
-    if (a < nrecw) rdst[a] = rw[q];
-  }
-  {
-    const uint64_t ob = __ballot(ov != 0);
-    if (lane == 0 && wid < 2) sm.rescan[wid] = ob;
-  }
-  __syncthreads();
 
   // ---- wave 0: row statistics, decision, group record, and the row bound
-  float M_t = NEG_INF, M_d = NEG_INF;
-  double S_t = 0.0, S_d = 0.0;
+  float M_t = NEG_INF;
   int fl = 0;
   if (wid == 0) {
-    const TileRec *R = sm.m.rec;
-    float am = NEG_INF, dm = NEG_INF;
-    int fa = 0, fd = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = lane + 64 * h;
-      if (t < nT) { am = fmaxf(am, R[t].m_t); dm = fmaxf(dm, R[t].m_d); fa |= R[t].flags_t; fd |= R[t].flags_d; }
-    }
-    M_t = wave_max_f(am);
-    M_d = pair ? wave_max_f(dm) : NEG_INF;
+    const float tm_t = __uint_as_float((uint32_t)rw[0]), tm_d = __uint_as_float((uint32_t)(rw[0] >> 32));
+    const double ts_t = __builtin_bit_cast(double, rw[1]), ts_d = __builtin_bit_cast(double, rw[2]);
+    int fa = own ? (int)(uint32_t)rw[3] : 0, fd = own ? (int)(uint32_t)(rw[3] >> 32) : 0;
+    M_t = wave_max_f(own ? tm_t : NEG_INF);
+    const float M_d = pair ? wave_max_f(own ? tm_d : NEG_INF) : NEG_INF;
     fa = wave_or(fa);
     fd = pair ? wave_or(fd) : 0;
+    double S_t = 0.0, S_d = 0.0;
     if (!GREEDY) {
-      double a = 0.0, d = 0.0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = lane + 64 * h;
-        if (t < nT) {
-          a += rescale(R[t].s_t, R[t].m_t, M_t, P.sc);
-          if (pair) d += rescale(R[t].s_d, R[t].m_d, M_d, P.sc);
-        }
-      }
-      S_t = wave_sum_d(a);
-      if (pair) S_d = wave_sum_d(d);
+      S_t = wave_sum_d(own ? rescale(ts_t, tm_t, M_t, P.sc) : 0.0);
+      if (pair) S_d = wave_sum_d(own ? rescale(ts_d, tm_d, M_d, P.sc) : 0.0);
     }
     // one data-error bit per row: NaN before +inf before an empty row
     fa = (fa & SV_STATUS_NAN) ? SV_STATUS_NAN : fa;
@@ -757,7 +884,7 @@ __device__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm)
           const double p = readlane_d(pv, 0), q = readlane_d(pv, 1);
           const double ratio = q > 0.0 ? p / q : (p > 0.0 ? __builtin_inf() : 0.0);
           const double a = ratio < 1.0 ? ratio : 1.0;
-          acc = ((double)__builtin_bit_cast(float, readlane(__float_as_uint(ui), 0)) < a) ? 1 : 0;
+          acc = ((double)__uint_as_float(readlane(__float_as_uint(ui), 0)) < a) ? 1 : 0;
         } else {
           acc = 0;
         }
@@ -775,45 +902,33 @@ __device__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm)
         if (dst) dst[(int64_t)b * k + i] = (float)pv;
         if (lane == 1 && P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)M_d / (double)P.T + lg);
       }
-      // row k: tile masses of p_k for a bonus draw
-      if (i == k) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int t = lane + 64 * h;
-          if (t < nT) st_dev(P.psum + (int64_t)b * nT + t, rescale(R[t].s_t, R[t].m_t, M_t, P.sc) / S_t);
-        }
-      }
+      // row k: the tile masses of p_k, for a bonus draw
+      if (i == k && own) st_dev(P.psum + (int64_t)b * nT + lane, rescale(ts_t, tm_t, M_t, P.sc) / S_t);
     }
 
-    // the row bound rb: the 32nd largest of the tiles' lane maxima (0 when
-    // there are fewer), found bit by bit from the top
-    const int ntops = nT * LIST, nq = (ntops + 63) >> 6;
-    uint32_t tops[TOPS_PL];
+    // the row bound rb: the 32nd largest of the tiles' lane maxima on 16-bit
+    // buckets (0 when there are fewer than 32), found bit by bit from the top
+    uint32_t top[LIST];
 #pragma unroll
-    for (int q = 0; q < TOPS_PL; ++q) {
-      const int f = lane + 64 * q;
-      tops[q] = (q < nq && f < ntops) ? R[f / LIST].top[f % LIST] : 0u;
+    for (int q = 0; q < LIST / 2; ++q) {
+      top[2 * q] = (uint32_t)rw[4 + q];
+      top[2 * q + 1] = (uint32_t)(rw[4 + q] >> 32);
     }
-    uint32_t prefix = 0;
-    for (int bit = 31; bit >= 32 - Fmt<DT>::BITS; --bit) {
-      const uint32_t cand = prefix | (1u << bit);
+    uint32_t rb = 0;
+    for (int bit = 31; bit >= 16; --bit) {
+      const uint32_t c = rb | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int q = 0; q < TOPS_PL; ++q)
-        if (q < nq) cnt += __popcll(__ballot(tops[q] >= cand));
-      if (cnt >= TOPK) prefix = cand;
+      for (int q = 0; q < LIST; ++q) cnt += __popcll(__ballot(top[q] >= c));
+      if (cnt >= TOPK) rb = c;
     }
-    // tiles to rescan: candidates overflowed, or the 8th lane maximum lies above
-    // the bound (elements between the two were not published)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = lane + 64 * h;
-      const uint64_t sat = __ballot(t < nT && R[t].top[LIST - 1] > (prefix | LOW));
-      if (lane == 0) sm.rescan[h] |= sat;
-    }
+    // tiles to rescan: candidates overflowed, or the candidate threshold lies in
+    // a bucket above the bound (elements between the two were not published)
+    const uint64_t rs = __ballot(own && (ov != 0 || top[LIST - 1] > (rb | 0xffffu)));
     if (lane == 0) {
+      sm.rescan = rs;
       sm.bc[0] = 0;
-      sm.bc[1] = (int)prefix;
+      sm.bc[1] = (int)rb;
       sm.bc[2] = fa;                           // the target row's own flags decide its top-32
       sm.bc[6] = -1;
     }
@@ -821,41 +936,35 @@ __device__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm)
   __syncthreads();
   const uint32_t rb = (uint32_t)sm.bc[1];
   const bool nanrow = (sm.bc[2] & SV_STATUS_NAN) != 0;
-  const uint64_t rs0 = sm.rescan[0], rs1 = sm.rescan[1];
+  const uint64_t rs = sm.rescan;
 
   // ---- candidates at or above the bound: slots of complete tiles, then rescans
   if (!nanrow) {
 #pragma unroll
     for (int q = 0; q < KEYS_PT; ++q) {
       const int a = tid + q * TPB;
-      if (a < nslot && key[q]) {
-        const int tc = a / SLOTS;
-        const bool skip = ((tc < 64 ? rs0 >> tc : rs1 >> (tc - 64)) & 1u) != 0;
-        if (!skip && (uint32_t)(key[q] >> 32) >= rb) {
-          const int pos = atomicAdd(&sm.bc[0], 1);
-          if (pos < MERGE_CAP) sm.m.keys[pos] = key[q];
-        }
+      if (a < nslot && key[q] && !((rs >> (a / SLOTS)) & 1u) && (uint32_t)(key[q] >> 32) >= rb) {
+        const int pos = atomicAdd(&sm.bc[0], 1);
+        if (pos < MERGE_CAP) sm.keys[pos] = key[q];
       }
     }
-    for (int h = 0; h < 2; ++h) {
-      uint64_t m = h ? rs1 : rs0;
-      while (m) {
-        const int tc = 64 * h + __builtin_ctzll(m);
-        m &= m - 1;
-        u32x4 r[NSEG];
-        load_tile<DT>(G.trow, tc, V, P.t_vec, r);
-        const int lim = V - tc * Fmt<DT>::TILE;
+    uint64_t m = rs;
+    while (m) {
+      const int tc = __builtin_ctzll(m);
+      m &= m - 1;
+      u32x4 r[NSEG];
+      load_tile<DT>(G.trow, tc, V, P.t_vec, r);
+      const int lim = V - tc * Fmt<DT>::TILE;
 #pragma unroll
-        for (int s = 0; s < NSEG; ++s)
+      for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-          for (int w = 0; w < Fmt<DT>::W; ++w) {
-            const float xv = unpack<DT>(r[s], w);
-            if (tpos<DT>(s, w) < lim && xv == xv && ordered_key(xv) >= rb) {
-              const int pos = atomicAdd(&sm.bc[0], 1);
-              if (pos < MERGE_CAP) sm.m.keys[pos] = cand_key(xv, tc * Fmt<DT>::TILE + tpos<DT>(s, w));
-            }
+        for (int w = 0; w < Fmt<DT>::W; ++w) {
+          const float xv = unpack<DT>(r[s], w);
+          if (tpos<DT>(s, w) < lim && xv == xv && ordered_key(xv) >= rb) {
+            const int pos = atomicAdd(&sm.bc[0], 1);
+            if (pos < MERGE_CAP) sm.keys[pos] = cand_key(xv, tc * Fmt<DT>::TILE + tpos<DT>(s, w));
           }
-      }
+        }
     }
   }
   __syncthreads();
@@ -868,9 +977,9 @@ __device__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm)
     topk_exact<DT>(G.trow, V, oval, oidx, sm);
   } else {
     for (int a = tid; a < n; a += TPB) {
-      const uint64_t ka = sm.m.keys[a];
+      const uint64_t ka = sm.keys[a];
       int rank = 0;
-      for (int jj = 0; jj < n; ++jj) rank += sm.m.keys[jj] > ka;
+      for (int jj = 0; jj < n; ++jj) rank += sm.keys[jj] > ka;
       if (rank < TOPK) {
         oidx[rank] = cand_index(ka);
         oval[rank] = cand_value(ka);
@@ -886,29 +995,33 @@ __device__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm)
     gr.flags = fl; gr.accept = 1; gr.argmax = sm.bc[6]; gr.pad = 0;
     st_rec(P.grec + g, gr);
   }
-  const int olds = arrive(P.sarrive + b, sm);
-
-  // every workgroup of the group has published and left: clear the group's
-  // workspace (nothing in this launch reads it again)
+  // the group record is out: announce it, then clear the group's workspace
+  // (nothing in this launch reads it again)
+  block_stores_done();
+  if (i != k && tid == 0) add_dev_noret(P.sarrive + b, 1);
 #pragma unroll
   for (int q = 0; q < KEYS_PT; ++q) {
     const int a = tid + q * TPB;
     if (a < nslot && key[q]) st_dev(slots + a, (uint64_t)0);
   }
+  if (own) {
 #pragma unroll
-  for (int q = 0; q < RECW_PT; ++q) {
-    const int a = tid + q * TPB;
-    if (a < nrecw && rw[q]) st_dev((uint64_t *)rsrc + a, (uint64_t)0);
+    for (int q = 0; q < 8; ++q) st_dev(rsrc + q, (uint64_t)0);
+    if (ov) st_dev(P.ovf + (int64_t)g * nT + lane, 0);
   }
-  if (ov) st_dev(P.ovf + (int64_t)g * nT + tid, 0);
-  if (tid == 0) st_dev(P.garrive + g, 0);
-
-  if (olds < 0 || olds > k) { if (tid == 0) atomicOr(P.fault, 2); return; }  // workspace not zero-filled
-  if (olds == k) seq_finish<GREEDY>(P, b, sm);
+  if (i != k) return;
+  // row k is the sequence's last group: wait for the others, then assemble
+  if (tid == 0) {
+    const int v = wait_at_least(P.sarrive + b, k, P.fault);
+    if (v > k) atomicOr(P.fault, 2);                                 // workspace not zero-filled
+    st_dev(P.sarrive + b, 0);
+  }
+  __syncthreads();
+  seq_finish<DT, GREEDY>(P, b, sm);
 }
 
 template <int DT, bool GREEDY>
-__global__ __launch_bounds__(TPB) void sv_stream(Params P) {
+__global__ __launch_bounds__(TPB) void sv_verify(Params P) {
   __shared__ Smem sm;
   constexpr int W = Fmt<DT>::W, TILE = Fmt<DT>::TILE;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -917,65 +1030,72 @@ __global__ __launch_bounds__(TPB) void sv_stream(Params P) {
   const Geo G = geo<DT, GREEDY>(P, item);
   const int c = G.c;
   const bool pair = G.pair;
-  // the drafted token of a pair group (used only by the group's last workgroup)
+  // the drafted token of a pair group (used only by the group's merge)
   const int32_t xtok = pair ? P.tokens[(int64_t)G.b * P.k + G.i] : -1;
 
   u32x4 rt[NSEG], rd[NSEG];
   load_tile<DT>(G.trow, c, V, P.t_vec, rt);
   if (pair) load_tile<DT>(G.drow, c, V, P.d_vec, rd);
-  else
-#pragma unroll
-    for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
   if (tid == 0) sm.bc[0] = 0;                          // candidate count
 
-  // per-thread statistics
+  // thread and wave statistics: maxima, then exp sums relative to the wave max
   const float mt = thread_max<DT>(rt);
-  const float md = pair ? thread_max<DT>(rd) : NEG_INF;
+  const float wm_t = wave_max_f(mt);
+  float wm_d = NEG_INF;
+  double ws_t = 0.0, ws_d = 0.0;
   int ft = 0, fd = 0;
-  float st = 0.f, sd = 0.f;
   if (!GREEDY) {
-    st = thread_expsum<DT>(rt, mt, P.sc, ft);
-    if (pair) sd = thread_expsum<DT>(rd, md, P.sc, fd);
+    const float st = thread_expsum<DT>(rt, wm_t == NEG_INF ? 0.f : wm_t, P.sc, ft);
+    ws_t = wave_sum_d((double)st);
+    if (pair) {
+      const float md = thread_max<DT>(rd);
+      wm_d = wave_max_f(md);
+      const float sd = thread_expsum<DT>(rd, wm_d == NEG_INF ? 0.f : wm_d, P.sc, fd);
+      ws_d = wave_sum_d((double)sd);
+    }
   } else {
     ft = thread_has_nan<DT>(rt) ? SV_STATUS_NAN : 0;
   }
+  const int wf_t = (__ballot(ft & SV_STATUS_NAN) ? SV_STATUS_NAN : 0) |
+                   (__ballot(ft & SV_STATUS_POSINF) ? SV_STATUS_POSINF : 0);
+  const int wf_d = (__ballot(fd & SV_STATUS_NAN) ? SV_STATUS_NAN : 0) |
+                   (__ballot(fd & SV_STATUS_POSINF) ? SV_STATUS_POSINF : 0);
+
+  // the wave's list of largest lane maxima
   const bool has_elem = (int64_t)c * TILE + (int64_t)tid * W < V;
   const uint32_t tkey = has_elem ? ordered_key(mt) : 0u;
-
-  // per-wave partials: max, sum relative to the wave max, flags, largest lane maxima
   {
-    const float wm_t = wave_max_f(mt);
-    const float wm_d = pair ? wave_max_f(md) : NEG_INF;
-    const int wf_t = wave_or(ft), wf_d = pair ? wave_or(fd) : 0;
-    double ws_t = 0.0, ws_d = 0.0;
-    if (!GREEDY) {
-      ws_t = wave_sum_d(rescale((double)st, mt, wm_t, P.sc));
-      if (pair) ws_d = wave_sum_d(rescale((double)sd, md, wm_d, P.sc));
-    }
-    const uint32_t w8 = wave_top_list(tkey, lane);
-    if (lane < LIST) sm.w8[wid * LIST + lane] = w8;
+    const uint32_t Kw = list_bound(tkey);
+    int n;
+    const int p = list_pos(tkey, Kw, lane, &n);
+    if (p >= 0) sm.w8[wid * LIST + p] = tkey;
+    if (lane >= n && lane < LIST) sm.w8[wid * LIST + lane] = 0u;
     if (lane == 0) {
       sm.f[0][wid] = wm_t; sm.f[1][wid] = wm_d; sm.i[0][wid] = wf_t; sm.i[1][wid] = wf_d;
       sm.d[0][wid] = ws_t; sm.d[1][wid] = ws_d;
     }
   }
   __syncthreads();
-  // the tile's largest lane maxima (every wave derives them) and the candidate bound
-  const uint32_t t8 = wave_top_list(lane < NWAVE * LIST ? sm.w8[lane] : 0u, lane);
-  const uint32_t bound = readlane(t8, LIST - 1);
+  // the tile's list (every wave derives its bound) and the candidate threshold
+  const uint32_t lk = lane < NWAVE * LIST ? sm.w8[lane] : 0u;
+  const uint32_t K8 = list_bound(lk);
 
-  // candidates: elements at or above the bound (all of a tile with fewer lanes)
+  // candidates: elements in or above the threshold's bucket (all of a tile
+  // with fewer than LIST lanes)
   {
-    const float Lf = key_value(bound);
+    // the bucket floor as a float; the bucket of -inf has no float floor (its
+    // floor pattern is a NaN), so every non-NaN element is in or above it
+    const float kv = key_value(K8);
+    const float thr = kv == kv ? kv : NEG_INF;
     const int lim = V - c * TILE;                        // tile positions < lim exist
     uint32_t mask = 0;
-    if (has_elem && (bound == 0u || tkey >= bound)) {
+    if (has_elem && (K8 == 0u || tkey >= K8)) {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s)
 #pragma unroll
         for (int w = 0; w < W; ++w) {
           const float xv = unpack<DT>(rt[s], w);
-          if (tpos<DT>(s, w) < lim && (bound == 0u || xv >= Lf)) mask |= 1u << (s * W + w);
+          if (tpos<DT>(s, w) < lim && (K8 == 0u || xv >= thr)) mask |= 1u << (s * W + w);
         }
     }
     const int cnt = __popc(mask);
@@ -994,8 +1114,12 @@ __global__ __launch_bounds__(TPB) void sv_stream(Params P) {
     }
   }
 
-  // the tile record (wave 0, from the four wave partials)
+  // the tile record (wave 0: lanes 0-7 write one word each)
   if (wid == 0) {
+    int n;
+    const int p = list_pos(lk, K8, lane, &n);
+    if (p >= 0) sm.t8[p] = lk;
+    if (lane >= n && lane < LIST) sm.t8[lane] = 0u;
     float m_ct = sm.f[0][0], m_cd = sm.f[1][0];
     int f_ct = sm.i[0][0], f_cd = sm.i[1][0];
     for (int w = 1; w < NWAVE; ++w) {
@@ -1008,109 +1132,42 @@ __global__ __launch_bounds__(TPB) void sv_stream(Params P) {
         s_ct += rescale(sm.d[0][w], sm.f[0][w], m_ct, P.sc);
         s_cd += rescale(sm.d[1][w], sm.f[1][w], m_cd, P.sc);
       }
-    TileRec r;
-    r.m_t = m_ct; r.m_d = m_cd; r.s_t = s_ct; r.s_d = s_cd; r.flags_t = f_ct; r.flags_d = f_cd;
-#pragma unroll
-    for (int q = 0; q < LIST; ++q) r.top[q] = readlane(t8, q);
-    if (lane == 0) st_rec(P.recs + item, r);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < 8) {
+      uint64_t word;
+      if (lane == 0) word = ((uint64_t)__float_as_uint(m_cd) << 32) | __float_as_uint(m_ct);
+      else if (lane == 1) word = __builtin_bit_cast(uint64_t, s_ct);
+      else if (lane == 2) word = __builtin_bit_cast(uint64_t, s_cd);
+      else if (lane == 3) word = ((uint64_t)(uint32_t)f_cd << 32) | (uint32_t)f_ct;
+      else word = ((uint64_t)sm.t8[2 * (lane - 4) + 1] << 32) | sm.t8[2 * (lane - 4)];
+      st_dev((uint64_t *)(P.recs + item) + lane, word);
+    }
   }
-  const int old = arrive(P.garrive + G.g, sm);
-  if (old < 0 || old >= P.nT) { if (tid == 0) atomicOr(P.fault, 2); return; }  // workspace not zero-filled
-  if (old != P.nT - 1) return;
+  block_stores_done();
+  if (c != P.nT - 1) {                                   // not the group's last tile: announce and leave
+    if (tid == 0) add_dev_noret(P.garrive + G.g, 1);
+    return;
+  }
+  // the group's last tile: wait for the other tiles, then merge
+  if (tid == 0) {
+    const int v = wait_at_least(P.garrive + G.g, P.nT - 1, P.fault);
+    if (v > P.nT - 1) atomicOr(P.fault, 2);                          // workspace not zero-filled
+    st_dev(P.garrive + G.g, 0);
+  }
+  __syncthreads();
   group_finish<DT, GREEDY>(P, G, xtok, sm);
 }
 
-// Inverse-CDF draw inside one tile: the first element (ascending index) of
-// positive mass whose cumulative mass prefix + (scan base + running fp32 sum)
-// exceeds tau; if rounding leaves none, the tile's last positive-mass element
-// (-1 when the tile has none).  The masses are recomputed exactly as when the
-// tile's total was published.
-template <int DT>
-__device__ int tile_draw(const Params &P, const char *trow, const char *drow, int c, bool resid, float m_t,
-                         double s_t, float m_d, double s_d, double prefix, double tau, Smem &sm) {
-  constexpr int W = Fmt<DT>::W;
-  u32x4 rt[NSEG], rd[NSEG];
-  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
-  if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
-  else
-#pragma unroll
-    for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
-  const float mt = thread_max<DT>(rt);
-  const float md = resid ? thread_max<DT>(rd) : NEG_INF;
-  const float at = prob_scale(mt, m_t, s_t, P.sc);
-  const float ad = resid ? prob_scale(md, m_d, s_d, P.sc) : 0.f;
-  float seg[NSEG];
-  seg_masses<DT>(rt, rd, resid, mt, md, at, ad, P.sc, seg);
-  double base[NSEG];
-  tile_scan(seg, base, sm);
-  int first = 0x7fffffff, lastpos = -1;
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    float a = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mval = elem_mass<DT>(rt[s], rd[s], w, resid, mt, md, at, ad, P.sc);
-      a += mval;
-      const int pos = tpos<DT>(s, w);
-      if (mval > 0.f) {
-        lastpos = pos > lastpos ? pos : lastpos;
-        if (prefix + (base[s] + (double)a) > tau && pos < first) first = pos;
-      }
-    }
-  }
-  first = wave_min_i(first);
-  lastpos = wave_max_i(lastpos);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  if (lane == 0) { sm.i[2][wid] = first; sm.i[3][wid] = lastpos; }
-  __syncthreads();
-  int f = sm.i[2][0], l = sm.i[3][0];
-  for (int w = 1; w < NWAVE; ++w) {
-    f = sm.i[2][w] < f ? sm.i[2][w] : f;
-    l = sm.i[3][w] > l ? sm.i[3][w] : l;
-  }
-  __syncthreads();
-  const int pos = f != 0x7fffffff ? f : l;
-  return pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
-}
-
-// Total target mass p of one tile (the arithmetic of tile_draw without a draft row).
-template <int DT>
-__device__ double tile_mass_p(const Params &P, const char *trow, int c, float m_t, double s_t, Smem &sm) {
-  u32x4 rt[NSEG];
-  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
-  const float mt = thread_max<DT>(rt);
-  const float at = prob_scale(mt, m_t, s_t, P.sc);
-  float seg[NSEG];
-  seg_masses<DT>(rt, rt, false, mt, NEG_INF, at, 0.f, P.sc, seg);
-  double base[NSEG];
-  return tile_scan(seg, base, sm);
-}
-
-// The crossing tile of tau = u * R over the tile masses in sm.tot (tile order,
-// R their sum): sm.bc[2] = the first tile whose cumulative mass exceeds tau (-1
-// if none), sm.dbc[0] = the mass before it, sm.dbc[1] = tau.  Run by wave 0.
-__device__ void locate_tile(int nT, double u, Smem &sm) {
-  const int lane = threadIdx.x & 63;
-  const double a0 = lane < nT ? sm.tot[lane] : 0.0;
-  const double a1 = lane + 64 < nT ? sm.tot[lane + 64] : 0.0;
-  const double c0 = wave_scan_d(a0);
-  const double t0 = readlane_d(c0, 63);
-  const double c1 = t0 + wave_scan_d(a1);
-  const double R = readlane_d(c1, 63);
-  const double tau = u * R;
-  const uint64_t h0 = __ballot(lane < nT && c0 > tau), h1 = __ballot(lane + 64 < nT && c1 > tau);
-  int cs = -1;
-  if (h0) cs = __builtin_ctzll(h0);
-  else if (h1) cs = 64 + __builtin_ctzll(h1);
-  double before = 0.0;
-  if (cs > 0) before = cs <= 64 ? readlane_d(c0, cs - 1) : readlane_d(c1, cs - 65);
-  if (lane == 0) { sm.bc[2] = cs; sm.dbc[0] = before; sm.dbc[1] = tau; }
-}
-
+// Draw workgroup (b, c).  Residual (rejection at j < k): publish tile c's
+// residual mass of pair row j; the last of the sequence's workgroups draws.
+// Bonus (k acceptances): workgroup 0 draws from p_k over the tile masses the
+// merge of row k published.  Every sequence's published masses are cleared.
 template <int DT>
 __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
   __shared__ Smem sm;
-  const int tid = threadIdx.x, wid = tid >> 6;
+  const int tid = threadIdx.x;
   const int nT = P.nT, k = P.k, K1 = k + 1;
   const int b = blockIdx.x / nT, c = blockIdx.x - (blockIdx.x / nT) * nT;
   const SeqRec sr = P.srec[b];
@@ -1119,6 +1176,10 @@ __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
   if (!sr.valid) return;
   const int j = sr.j;
   const bool resid = sr.resid != 0;
+  if (j < 0 || j > k || (resid && j == k)) {                       // workspace not zero-filled
+    if (tid == 0) atomicOr(P.fault, 2);
+    return;
+  }
   const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
   const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
   double *masses;
@@ -1143,41 +1204,14 @@ __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
     if (old != nT - 1) return;
     masses = P.rsum + (int64_t)b * nT;
   }
-
-  // locate the crossing tile in tile order, then rescan it
   for (int cc = tid; cc < nT; cc += TPB) sm.tot[cc] = ld_dev(masses + cc);
-  __syncthreads();
-  if (wid == 0) locate_tile(nT, sr.u, sm);
-  __syncthreads();
-  bool use_p = false;
-  if (sm.bc[2] < 0 && resid) {
-    // no residual mass left (only through rounding): draw from p_j with the same uniform
-    use_p = true;
-    for (int cc = 0; cc < nT; ++cc) {
-      const double m = tile_mass_p<DT>(P, trow, cc, sr.m_t, sr.s_t, sm);
-      if (tid == 0) sm.tot[cc] = m;
-    }
-    __syncthreads();
-    if (wid == 0) locate_tile(nT, sr.u, sm);
-    __syncthreads();
-  }
-  const int cstar = sm.bc[2] >= 0 ? sm.bc[2] : nT - 1;
-  const double prefix = sm.dbc[0], tau = sm.dbc[1];
-  __syncthreads();
-  const bool rmode = resid && !use_p;
-  int token = tile_draw<DT>(P, trow, drow, cstar, rmode, sr.m_t, sr.s_t, sr.m_d, sr.s_d, prefix, tau, sm);
-  // a tile whose recomputed masses all rounded to zero: the last positive-mass
-  // element before it
-  for (int cc = cstar - 1; token < 0 && cc >= 0; --cc)
-    token = tile_draw<DT>(P, trow, drow, cc, rmode, sr.m_t, sr.s_t, sr.m_d, sr.s_d, 0.0, __builtin_inf(), sm);
+  const int token = draw_row<DT>(P, trow, drow, resid, sr.m_t, sr.s_t, sr.m_d, sr.s_d, sr.u, sm);
   if (tid == 0) {
     P.out_tokens[(int64_t)b * K1 + j] = token;
     if (resid) st_dev(P.darrive + b, 0);
-    SeqRec z;
-    memset(&z, 0, sizeof z);
-    P.srec[b] = z;
   }
   for (int cc = tid; cc < nT; cc += TPB) st_dev(masses + cc, 0.0);
+  zero_recs(P.srec + b, 1);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1217,11 +1251,11 @@ bool shape_ok(const sv_shape_t *s) {
 template <int DT> hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
   const unsigned items = (unsigned)((int64_t)P.B * (P.k + 1) * P.nT);
   if (greedy) {
-    hipLaunchKernelGGL((sv_stream<DT, true>), dim3(items), dim3(TPB), 0, stream, P);
+    hipLaunchKernelGGL((sv_verify<DT, true>), dim3(items), dim3(TPB), 0, stream, P);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((sv_stream<DT, false>), dim3(items), dim3(TPB), 0, stream, P);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((sv_verify<DT, false>), dim3(items), dim3(TPB), 0, stream, P);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((sv_draw<DT>), dim3((unsigned)((int64_t)P.B * P.nT)), dim3(TPB), 0, stream, P);
   return hipGetLastError();
