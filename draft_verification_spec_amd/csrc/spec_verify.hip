@@ -61,7 +61,7 @@ constexpr int TPB = 256;               // threads per workgroup (4 waves of 64)
 constexpr int NWAVE = TPB / 64;
 constexpr int NSEG = 4;                // 16-byte vectors per thread per row
 constexpr int LIST = 8;                // lane maxima a tile record keeps
-constexpr int SLOTS = 16;              // candidate slots per tile
+constexpr int SLOTS = 32;              // candidate slots per tile
 constexpr int MERGE_CAP = 512;         // candidates a row merge ranks in LDS
 constexpr int TOPK = SV_TOPK;
 constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
@@ -71,18 +71,26 @@ constexpr uint64_t SPIN_TICKS = 20000000;          // bounded waits give up afte
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// E: bytes per element; W: elements per 16-byte vector; TILE: elements per tile
+// E: bytes per element; W: elements per 16-byte vector; TILE: elements per tile;
+// LOW: key bits below the 16-bit bucket that no element of the format can vary
 template <int DT> struct Fmt;
-template <> struct Fmt<SV_BF16> { static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8; };
-template <> struct Fmt<SV_F32> { static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4; };
+template <> struct Fmt<SV_BF16> {
+  static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8;
+  static constexpr uint32_t LOW = 0xffffu;   // low key bits of a bf16 value are all 0 or all 1
+};
+template <> struct Fmt<SV_F32> {
+  static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4;
+  static constexpr uint32_t LOW = 0u;
+};
 
 // Published per (group, tile) by the stream workgroups; 8 words.
 struct TileRec {
   float m_t, m_d;          // tile max of the target / draft row part
   double s_t, s_d;         // sum exp2((x - m) * sc) over the tile part
-  int32_t flags_t, flags_d;
-  uint32_t top[LIST];      // ordered keys of 8 largest lane maxima (0: no lane); top[7] lies
-                           // in the 16-bit bucket of the candidate threshold
+  int32_t flags;           // SV_STATUS_* bits: target row part | draft row part << 8
+  uint32_t kthr;           // ordered key of the candidate threshold (0: every element)
+  uint32_t top[LIST];      // ordered keys of 8 lane maxima of distinct lanes, the two
+                           // largest of each wave (0: no lane)
 };
 static_assert(sizeof(TileRec) == 64, "tile record");
 
@@ -136,8 +144,7 @@ struct Smem {
       uint64_t list[TOPK];
     } fb;
   };
-  uint32_t w8[NWAVE * LIST];           // stream: each wave's largest lane maxima
-  uint32_t t8[LIST];                   // stream: the tile's list
+  uint32_t w8[LIST];                   // stream: each wave's two largest lane maxima
   double tot[MAX_TILES];               // draw: tile masses in tile order
   float f[4][NWAVE];
   int32_t i[4][NWAVE];
@@ -235,32 +242,36 @@ __device__ __forceinline__ double wave_scan_d(double x) {
 // value of the previous lane of the wave (0 in lane 0)
 __device__ __forceinline__ double wave_prev_d(double v) { return dpp_d<0x138, 0xf, 0xf>(v); }
 
-// ---- lists of largest keys.  Keys are compared on their top 16 bits (a bf16
-// value's whole key; an fp32 key's sign, exponent and 7 mantissa bits).
-// The largest K = P << 16 such that at least LIST lanes hold a key >= K (0 when
-// fewer than LIST lanes hold a nonzero key).
-__device__ __forceinline__ uint32_t list_bound(uint32_t key) {
-  uint32_t K = 0;
-#pragma unroll
-  for (int bit = 31; bit >= 16; --bit) {
-    const uint32_t c = K | (1u << bit);
-    if (__popcll(__ballot(key >= c)) >= LIST) K = c;
+// The two largest keys of the wave's lanes (equal keys of different lanes
+// count twice; 0 where fewer lanes hold a nonzero key), in every lane.
+__device__ __forceinline__ void wave_top2(uint32_t key, uint32_t &k1, uint32_t &k2) {
+  uint32_t a = key, c = 0u;
+#define SV_TOP2_STEP(CTRL, RM, BM)                                   \
+  {                                                                   \
+    const uint32_t b = dpp<CTRL, RM, BM>(0u, a), d = dpp<CTRL, RM, BM>(0u, c); \
+    const uint32_t hi = a > b ? a : b, lo = a > b ? b : a;           \
+    c = lo > c ? lo : c;                                              \
+    c = d > c ? d : c;                                                \
+    a = hi;                                                           \
   }
-  return K;
+  SV_TOP2_STEP(0x111, 0xf, 0xf)
+  SV_TOP2_STEP(0x112, 0xf, 0xf)
+  SV_TOP2_STEP(0x114, 0xf, 0xe)
+  SV_TOP2_STEP(0x118, 0xf, 0xc)
+  SV_TOP2_STEP(0x142, 0xa, 0xf)
+  SV_TOP2_STEP(0x143, 0xc, 0xf)
+#undef SV_TOP2_STEP
+  k1 = readlane(a, 63);
+  k2 = readlane(c, 63);
 }
-// This lane's position in the wave's list of LIST largest keys under bound K:
-// keys above K's bucket first, then keys in it, each in lane order; -1 if the
-// key is not listed.  *n receives the list length (<= LIST).
-__device__ __forceinline__ int list_pos(uint32_t key, uint32_t K, int lane, int *n) {
-  const bool above = key != 0u && (key >> 16) > (K >> 16);
-  const bool tie = key != 0u && (key >> 16) == (K >> 16);
-  const uint64_t ma = __ballot(above), mt = __ballot(tie);
-  const uint64_t below = (1ull << lane) - 1ull;
-  const int a = __popcll(ma), len = a + __popcll(mt);
-  *n = len < LIST ? len : LIST;
-  if (above) return __popcll(ma & below);
-  if (tie) { const int p = a + __popcll(mt & below); return p < LIST ? p : -1; }
-  return -1;
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += __uint_as_float(dpp<0x111, 0xf, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<0x112, 0xf, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<0x114, 0xf, 0xe>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<0x118, 0xf, 0xc>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<0x142, 0xa, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<0x143, 0xc, 0xf>(0u, __float_as_uint(v)));
+  return __uint_as_float(readlane(__float_as_uint(v), 63));
 }
 
 // Device-scope accesses: loads see the latest device-visible value; stores are
@@ -716,11 +727,15 @@ __device__ __forceinline__ int draw_row(const Params &P, const char *trow, const
   const double prefix = sm.dbc[0], tau = sm.dbc[1];
   __syncthreads();
   const bool rmode = resid && !use_p;
-  int token = tile_draw<DT>(P, trow, drow, cstar, rmode, m_t, s_t, m_d, s_d, prefix, tau, sm);
-  // a tile whose recomputed masses all rounded to zero: the last positive-mass
-  // element before it
-  for (int cc = cstar - 1; token < 0 && cc >= 0; --cc)
-    token = tile_draw<DT>(P, trow, drow, cc, rmode, m_t, s_t, m_d, s_d, 0.0, __builtin_inf(), sm);
+  // the crossing tile; should its recomputed masses all round to zero, the
+  // last positive-mass element before it
+  int token = -1;
+  double pre = prefix, ta = tau;
+  for (int cc = cstar; token < 0 && cc >= 0; --cc) {
+    token = tile_draw<DT>(P, trow, drow, cc, rmode, m_t, s_t, m_d, s_d, pre, ta, sm);
+    pre = 0.0;
+    ta = __builtin_inf();
+  }
   return token;
 }
 
@@ -852,7 +867,8 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   if (wid == 0) {
     const float tm_t = __uint_as_float((uint32_t)rw[0]), tm_d = __uint_as_float((uint32_t)(rw[0] >> 32));
     const double ts_t = __builtin_bit_cast(double, rw[1]), ts_d = __builtin_bit_cast(double, rw[2]);
-    int fa = own ? (int)(uint32_t)rw[3] : 0, fd = own ? (int)(uint32_t)(rw[3] >> 32) : 0;
+    int fa = own ? (int)((uint32_t)rw[3] & 0xffu) : 0, fd = own ? (int)(((uint32_t)rw[3] >> 8) & 0xffu) : 0;
+    const uint32_t kthr = (uint32_t)(rw[3] >> 32);
     M_t = wave_max_f(own ? tm_t : NEG_INF);
     const float M_d = pair ? wave_max_f(own ? tm_d : NEG_INF) : NEG_INF;
     fa = wave_or(fa);
@@ -922,9 +938,9 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
       for (int q = 0; q < LIST; ++q) cnt += __popcll(__ballot(top[q] >= c));
       if (cnt >= TOPK) rb = c;
     }
-    // tiles to rescan: candidates overflowed, or the candidate threshold lies in
-    // a bucket above the bound (elements between the two were not published)
-    const uint64_t rs = __ballot(own && (ov != 0 || top[LIST - 1] > (rb | 0xffffu)));
+    // tiles to rescan: candidates overflowed, or the candidate threshold lies
+    // above the bound (elements between the two were not published)
+    const uint64_t rs = __ballot(own && (ov != 0 || kthr > (rb | Fmt<DT>::LOW)));
     if (lane == 0) {
       sm.rescan = rs;
       sm.bc[0] = 0;
@@ -1020,8 +1036,53 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   seq_finish<DT, GREEDY>(P, b, sm);
 }
 
+// The thread's elements of one tile row as fp32, vector by vector.
+template <int DT> struct Elems {
+  float x[NSEG][Fmt<DT>::W];
+};
+template <int DT> __device__ __forceinline__ void unpack_all(const u32x4 (&r)[NSEG], Elems<DT> &e) {
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+    for (int w = 0; w < Fmt<DT>::W; ++w) e.x[s][w] = unpack<DT>(r[s], w);
+}
+template <int DT> __device__ __forceinline__ float vmax_of(const Elems<DT> &e, int s) {
+  float m = e.x[s][0];
+#pragma unroll
+  for (int w = 1; w < Fmt<DT>::W; ++w) m = fmaxf(m, e.x[s][w]);
+  return m;
+}
+template <int DT> __device__ __forceinline__ bool has_nan_of(const Elems<DT> &e) {
+  bool nan = false;
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+    for (int w = 0; w < Fmt<DT>::W; ++w) nan |= !(e.x[s][w] == e.x[s][w]);
+  return nan;
+}
+
+// Wave statistics of one row part: the wave max wm and the sum of
+// exp2((x - wm) * sc) over the wave's elements (fp32 per thread and wave,
+// returned in fp64 with the rounding of wm * sc corrected); flags NaN / +inf.
+template <int DT>
+__device__ __forceinline__ void wave_stats(const Elems<DT> &e, float mt, float sc, float &wm, double &ws, int &flags) {
+  wm = wave_max_f(mt);
+  const float ref = wm == NEG_INF ? 0.f : wm;
+  const float chi = ref * sc, clo = fmaf(ref, sc, -chi);    // ref * sc = chi + clo exactly
+  float st = 0.f;
+#pragma unroll
+  for (int g = 0; g < NSEG; ++g)
+#pragma unroll
+    for (int w = 0; w < Fmt<DT>::W; ++w) st += __builtin_amdgcn_exp2f(fmaf(e.x[g][w], sc, -chi));
+  const bool bad = !(st == st);
+  flags = 0;
+  if (__ballot(bad)) flags = __ballot(bad && has_nan_of<DT>(e)) ? SV_STATUS_NAN : SV_STATUS_POSINF;
+  // exp2(x*sc - ref*sc) = exp2(x*sc - chi) * exp2(-clo), |clo| <= ulp(chi) / 2
+  ws = (double)wave_sum_f(st) * (1.0 - (double)clo * 0.69314718055994531);
+}
+
 template <int DT, bool GREEDY>
-__global__ __launch_bounds__(TPB) void sv_verify(Params P) {
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) void sv_verify(Params P) {
   __shared__ Smem sm;
   constexpr int W = Fmt<DT>::W, TILE = Fmt<DT>::TILE;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1038,64 +1099,64 @@ __global__ __launch_bounds__(TPB) void sv_verify(Params P) {
   if (pair) load_tile<DT>(G.drow, c, V, P.d_vec, rd);
   if (tid == 0) sm.bc[0] = 0;                          // candidate count
 
-  // thread and wave statistics: maxima, then exp sums relative to the wave max
-  const float mt = thread_max<DT>(rt);
-  const float wm_t = wave_max_f(mt);
-  float wm_d = NEG_INF;
+  // wave maxima, exp sums and flags: the draft part first (its elements are
+  // not needed afterwards), then the target part, each unpacked once
+  float wm_t, wm_d = NEG_INF;
   double ws_t = 0.0, ws_d = 0.0;
-  int ft = 0, fd = 0;
-  if (!GREEDY) {
-    const float st = thread_expsum<DT>(rt, wm_t == NEG_INF ? 0.f : wm_t, P.sc, ft);
-    ws_t = wave_sum_d((double)st);
-    if (pair) {
-      const float md = thread_max<DT>(rd);
-      wm_d = wave_max_f(md);
-      const float sd = thread_expsum<DT>(rd, wm_d == NEG_INF ? 0.f : wm_d, P.sc, fd);
-      ws_d = wave_sum_d((double)sd);
-    }
-  } else {
-    ft = thread_has_nan<DT>(rt) ? SV_STATUS_NAN : 0;
+  int wf_t = 0, wf_d = 0;
+  if (pair) {
+    Elems<DT> ed;
+    unpack_all<DT>(rd, ed);
+    float md = vmax_of<DT>(ed, 0);
+#pragma unroll
+    for (int s = 1; s < NSEG; ++s) md = fmaxf(md, vmax_of<DT>(ed, s));
+    wave_stats<DT>(ed, md, P.sc, wm_d, ws_d, wf_d);
   }
-  const int wf_t = (__ballot(ft & SV_STATUS_NAN) ? SV_STATUS_NAN : 0) |
-                   (__ballot(ft & SV_STATUS_POSINF) ? SV_STATUS_POSINF : 0);
-  const int wf_d = (__ballot(fd & SV_STATUS_NAN) ? SV_STATUS_NAN : 0) |
-                   (__ballot(fd & SV_STATUS_POSINF) ? SV_STATUS_POSINF : 0);
+  Elems<DT> et;
+  unpack_all<DT>(rt, et);
+  float vmt[NSEG];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) vmt[s] = vmax_of<DT>(et, s);
+  float mt = vmt[0];
+#pragma unroll
+  for (int s = 1; s < NSEG; ++s) mt = fmaxf(mt, vmt[s]);
+  if (!GREEDY) {
+    wave_stats<DT>(et, mt, P.sc, wm_t, ws_t, wf_t);
+  } else {
+    wm_t = wave_max_f(mt);
+    wf_t = __ballot(has_nan_of<DT>(et)) ? SV_STATUS_NAN : 0;   // the maxima skip NaN: test every element
+  }
 
-  // the wave's list of largest lane maxima
+  // the wave's two largest lane maxima
   const bool has_elem = (int64_t)c * TILE + (int64_t)tid * W < V;
   const uint32_t tkey = has_elem ? ordered_key(mt) : 0u;
-  {
-    const uint32_t Kw = list_bound(tkey);
-    int n;
-    const int p = list_pos(tkey, Kw, lane, &n);
-    if (p >= 0) sm.w8[wid * LIST + p] = tkey;
-    if (lane >= n && lane < LIST) sm.w8[wid * LIST + lane] = 0u;
-    if (lane == 0) {
-      sm.f[0][wid] = wm_t; sm.f[1][wid] = wm_d; sm.i[0][wid] = wf_t; sm.i[1][wid] = wf_d;
-      sm.d[0][wid] = ws_t; sm.d[1][wid] = ws_d;
-    }
+  uint32_t k1, k2;
+  wave_top2(tkey, k1, k2);
+  if (lane == 0) {
+    sm.w8[2 * wid] = k1; sm.w8[2 * wid + 1] = k2;
+    sm.f[0][wid] = wm_t; sm.f[1][wid] = wm_d; sm.i[0][wid] = wf_t; sm.i[1][wid] = wf_d;
+    sm.d[0][wid] = ws_t; sm.d[1][wid] = ws_d;
   }
   __syncthreads();
-  // the tile's list (every wave derives its bound) and the candidate threshold
-  const uint32_t lk = lane < NWAVE * LIST ? sm.w8[lane] : 0u;
-  const uint32_t K8 = list_bound(lk);
+  // the candidate threshold: the smallest nonzero of the tile's 8 lane maxima
+  // (8 distinct lanes hold an element at or above it); 0 in an empty tile
+  uint32_t kthr = 0xffffffffu;
+#pragma unroll
+  for (int q = 0; q < LIST; ++q) { const uint32_t v = sm.w8[q]; if (v && v < kthr) kthr = v; }
+  if (kthr == 0xffffffffu) kthr = 0u;
 
-  // candidates: elements in or above the threshold's bucket (all of a tile
-  // with fewer than LIST lanes)
+  // candidates: elements at or above the threshold, to this tile's slots
   {
-    // the bucket floor as a float; the bucket of -inf has no float floor (its
-    // floor pattern is a NaN), so every non-NaN element is in or above it
-    const float kv = key_value(K8);
-    const float thr = kv == kv ? kv : NEG_INF;
+    const float thr = key_value(kthr);
     const int lim = V - c * TILE;                        // tile positions < lim exist
     uint32_t mask = 0;
-    if (has_elem && (K8 == 0u || tkey >= K8)) {
+    if (has_elem && tkey >= kthr) {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s)
+        if (vmt[s] >= thr) {
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-          const float xv = unpack<DT>(rt[s], w);
-          if (tpos<DT>(s, w) < lim && (K8 == 0u || xv >= thr)) mask |= 1u << (s * W + w);
+          for (int w = 0; w < W; ++w)
+            if (tpos<DT>(s, w) < lim && et.x[s][w] >= thr) mask |= 1u << (s * W + w);
         }
     }
     const int cnt = __popc(mask);
@@ -1103,12 +1164,18 @@ __global__ __launch_bounds__(TPB) void sv_verify(Params P) {
       const int base = atomicAdd(&sm.bc[0], cnt);
       uint64_t *dst = P.cand + (int64_t)item * SLOTS;
       int slot = base;
-      while (mask) {
-        const int bit = __builtin_ctz(mask);
-        mask &= mask - 1;
-        const int s = bit / W, w = bit - s * W;
-        if (slot < SLOTS) st_dev(dst + slot, cand_key(unpack<DT>(rt[s], w), c * TILE + tpos<DT>(s, w)));
-        ++slot;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) {
+        uint32_t m = (mask >> (s * W)) & ((1u << W) - 1u);
+        while (m) {
+          const int w = __builtin_ctz(m);
+          m &= m - 1;
+          float xv = et.x[s][0];                         // element w, by selection (no indexed registers)
+#pragma unroll
+          for (int q = 1; q < W; ++q) xv = w == q ? et.x[s][q] : xv;
+          if (slot < SLOTS) st_dev(dst + slot, cand_key(xv, c * TILE + tpos<DT>(s, w)));
+          ++slot;
+        }
       }
       if (base + cnt > SLOTS) st_dev(P.ovf + item, 1);
     }
@@ -1116,10 +1183,6 @@ __global__ __launch_bounds__(TPB) void sv_verify(Params P) {
 
   // the tile record (wave 0: lanes 0-7 write one word each)
   if (wid == 0) {
-    int n;
-    const int p = list_pos(lk, K8, lane, &n);
-    if (p >= 0) sm.t8[p] = lk;
-    if (lane >= n && lane < LIST) sm.t8[lane] = 0u;
     float m_ct = sm.f[0][0], m_cd = sm.f[1][0];
     int f_ct = sm.i[0][0], f_cd = sm.i[1][0];
     for (int w = 1; w < NWAVE; ++w) {
@@ -1132,16 +1195,13 @@ __global__ __launch_bounds__(TPB) void sv_verify(Params P) {
         s_ct += rescale(sm.d[0][w], sm.f[0][w], m_ct, P.sc);
         s_cd += rescale(sm.d[1][w], sm.f[1][w], m_cd, P.sc);
       }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (lane < 8) {
       uint64_t word;
       if (lane == 0) word = ((uint64_t)__float_as_uint(m_cd) << 32) | __float_as_uint(m_ct);
       else if (lane == 1) word = __builtin_bit_cast(uint64_t, s_ct);
       else if (lane == 2) word = __builtin_bit_cast(uint64_t, s_cd);
-      else if (lane == 3) word = ((uint64_t)(uint32_t)f_cd << 32) | (uint32_t)f_ct;
-      else word = ((uint64_t)sm.t8[2 * (lane - 4) + 1] << 32) | sm.t8[2 * (lane - 4)];
+      else if (lane == 3) word = ((uint64_t)kthr << 32) | (uint32_t)(f_ct | (f_cd << 8));
+      else word = ((uint64_t)sm.w8[2 * (lane - 4) + 1] << 32) | sm.w8[2 * (lane - 4)];
       st_dev((uint64_t *)(P.recs + item) + lane, word);
     }
   }
