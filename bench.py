@@ -8,9 +8,11 @@ Cache) rotate so every step reads its logits from HBM.
 
 Prints one JSON line.  value = algorithmic logit bytes (each logit read once,
 B(2k+1)V * 2 bytes) / wall time per step, inputs resident in HBM.  roofline =
-the same bytes / the kernel's own duration (HIP events around each launch on
-the launch stream) against the 8 TB/s HBM peak.  cpu_baseline = the plain C
-oracle on the host over the same batch.
+the same bytes / the duration of the streaming kernel sv_verify, the one that
+reads every logit (HIP events the library records right before and after it
+on the launch stream), against the 8 TB/s HBM peak.  The step also runs the
+small draw kernel.  cpu_baseline = the plain C oracle on the host over a
+bounded number of whole batches.
 
   python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|tiny]
   python bench.py --copy-calib    # a plain 1 GiB device copy, for HBM counter calibration
@@ -51,6 +53,24 @@ def make_workload(name):
 
 def describe(w):
     return f"{w.name} B={w.B} k={w.k} V={w.V} {'bf16' if w.dtype else 'f32'} T={w.temperature:g}"
+
+
+def counted_traffic(w):
+    """HBM bytes per sv_verify launch from the committed rocprofv3 counter
+    summary of this workload (fetched + written, copy-calibrated), or None when
+    there is none or the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    name = f"sv_verify_{w.name}_B{w.B}_k{w.k}_V{w.V}_{'bf16' if w.dtype else 'f32'}.md"
+    path = os.path.join(ROOT, "profiles", name)
+    src = os.path.join(ROOT, "draft_verification_spec_amd", "csrc", "spec_verify.hip")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"traffic_per_launch: source_sha256=([0-9a-f]{64}) fetch_bytes=(\d+) write_bytes=(\d+)",
+                  open(path).read())
+    if not m or hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(1):
+        return None
+    return int(m.group(2)) + int(m.group(3))
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -114,10 +134,10 @@ def main():
     ws = sv.workspace_for(t.device, sv.spec_verify_workspace_bytes(shape))
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i, events=None):
         tt, dd, xx, uu = sets[i % copies]
         return sv.verify(tt, None if greedy else dd, xx, None if greedy else uu, w.temperature,
-                         workspace=ws, stream=stream.cuda_stream)
+                         workspace=ws, stream=stream.cuda_stream, events=events)
 
     for i in range(args.warmup):
         step(i)
@@ -125,13 +145,14 @@ def main():
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps over {copies} input copies",
           file=sys.stderr, flush=True)
 
-    # kernel duration: an event pair around each launch on the launch stream
+    # streaming-kernel duration: the library records an event pair around it on the launch stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:                      # torch creates the underlying events on first record
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(args.warmup + i)
-        ev[i][1].record(stream)
+        step(args.warmup + i, events=ev[i])
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
@@ -160,7 +181,7 @@ def main():
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(w),
                      "kernel": "sv_verify", "kernel_us_mean": round(kern_avg * 1e3, 3),
                      "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, q)) * 1e3, 3) for q in (10, 50, 90)]},
         "mean_accepted_len": float(np.mean(g["accepted_len"])),

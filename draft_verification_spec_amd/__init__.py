@@ -34,7 +34,8 @@ class sv_shape_t(ctypes.Structure):
 
 class sv_aux_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_void_p), ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p),
-                ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p)]
+                ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p),
+                ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -126,12 +127,14 @@ def _row_stride(t, rows_per_seq):
 
 
 def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bool = False,
-           workspace=None, stream=None) -> Result:
+           workspace=None, stream=None, events=None) -> Result:
     """Verify on torch tensors of one device.
 
     target [B,k+1,V] and draft [B,k,V] (float32 or bfloat16, same dtype; draft
     may be None when temperature == 0), draft_tokens [B,k] int32, uniforms
-    [B,k+2] float32 (None allowed when temperature == 0).  Returns device tensors.
+    [B,k+2] float32 (None allowed when temperature == 0).  events: optional
+    pair of torch.cuda.Event recorded right before and after the streaming
+    kernel on the launch stream.  Returns device tensors.
     """
     import torch
     if target.dim() != 3:
@@ -176,14 +179,16 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bo
     tv = torch.empty(B, K1, TOPK, **f32)
     ti = torch.empty(B, K1, TOPK, **i32)
     st = torch.empty(B, **i32)
-    a = sv_aux_t(st.data_ptr(), None, None, None, None)
+    a = sv_aux_t(st.data_ptr(), None, None, None, None, None, None)
     lt = ld = pt = qt = None
     if aux and not greedy:
         lt = torch.empty(B, K1, **f32)
         ld = torch.empty(B, k, **f32)
         pt = torch.empty(B, k, **f32)
         qt = torch.empty(B, k, **f32)
-        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr())
+        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr(), None, None)
+    if events is not None:
+        a.event_begin, a.event_end = events[0].cuda_event, events[1].cuda_event
     nbytes = spec_verify_workspace_bytes(shape)
     ws = workspace if workspace is not None else workspace_for(dev, nbytes)
     if stream is None:

@@ -1308,15 +1308,16 @@ bool shape_ok(const sv_shape_t *s) {
          (int64_t)s->V <= (int64_t)MAX_TILES * tile_of(s->dtype);
 }
 
-template <int DT> hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
+template <int DT>
+hipError_t launch(const Params &P, bool greedy, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const unsigned items = (unsigned)((int64_t)P.B * (P.k + 1) * P.nT);
-  if (greedy) {
-    hipLaunchKernelGGL((sv_verify<DT, true>), dim3(items), dim3(TPB), 0, stream, P);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((sv_verify<DT, false>), dim3(items), dim3(TPB), 0, stream, P);
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipErrorInvalidValue;
+  if (greedy) hipLaunchKernelGGL((sv_verify<DT, true>), dim3(items), dim3(TPB), 0, stream, P);
+  else hipLaunchKernelGGL((sv_verify<DT, false>), dim3(items), dim3(TPB), 0, stream, P);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return hipErrorInvalidValue;
+  if (greedy) return hipSuccess;
   hipLaunchKernelGGL((sv_draw<DT>), dim3((unsigned)((int64_t)P.B * P.nT)), dim3(TPB), 0, stream, P);
   return hipGetLastError();
 }
@@ -1407,7 +1408,9 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   P.t_vec = (((uintptr_t)target_logits & 15) == 0 && ((ts * esz) & 15) == 0) ? 1 : 0;
   P.d_vec = (!greedy && s.k > 0 && ((uintptr_t)draft_logits & 15) == 0 && ((ds * esz) & 15) == 0) ? 1 : 0;
 
-  const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, (hipStream_t)stream)
-                                          : launch<SV_F32>(P, greedy, (hipStream_t)stream);
+  const hipEvent_t ev0 = aux ? (hipEvent_t)aux->event_begin : nullptr;
+  const hipEvent_t ev1 = aux ? (hipEvent_t)aux->event_end : nullptr;
+  const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, (hipStream_t)stream, ev0, ev1)
+                                          : launch<SV_F32>(P, greedy, (hipStream_t)stream, ev0, ev1);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

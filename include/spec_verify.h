@@ -57,7 +57,7 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
 #define SV_ERR_DTYPE (-4)       /* dtype not SV_F32 / SV_BF16 */
 #define SV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than spec_verify_workspace_bytes */
 #define SV_ERR_HIP (-6)         /* a HIP runtime call or the kernel launch failed */
-#define SV_ERR_DEVICE (-7)      /* current device is not usable (no cooperative launch) */
+#define SV_ERR_DEVICE (-7)      /* current device is not usable */
 
 /* per-sequence data-error bits written to aux->status (device side) */
 #define SV_STATUS_BAD_TOKEN 1    /* a draft token is outside [0, V) */
@@ -65,7 +65,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
 #define SV_STATUS_POSINF 4       /* sampling: a used row holds +inf (softmax undefined) */
 #define SV_STATUS_EMPTY_ROW 8    /* sampling: a used row is all -inf (no distribution) */
 #define SV_STATUS_BAD_UNIFORM 16 /* sampling: a uniform is outside [0, 1) */
-#define SV_STATUS_SYNC_TIMEOUT 32 /* internal: a cross-workgroup wait gave up (never expected) */
+#define SV_STATUS_SYNC_TIMEOUT 32 /* internal: a bounded cross-workgroup wait gave up, or the
+                                     workspace was not zero-filled (never expected) */
 
 typedef struct {
     int32_t B;                  /* sequences, >= 0 (0: nothing to do) */
@@ -85,6 +86,9 @@ typedef struct {
     float *lse_draft;    /* [B,k]   ln sum_x exp(d_x / T)   (sampling only) */
     float *p_tok;        /* [B,k]   p_i(x_i)                (sampling only) */
     float *q_tok;        /* [B,k]   q_i(x_i)                (sampling only) */
+    void *event_begin;   /* hipEvent_t recorded on the stream right before the streaming
+                            kernel (the one that reads every logit), or NULL */
+    void *event_end;     /* hipEvent_t recorded right after it (before the draw kernel), or NULL */
 } sv_aux_t;
 
 /* Bytes of device workspace one call with this shape needs. */
@@ -119,6 +123,10 @@ size_t spec_verify_workspace_bytes(const sv_shape_t *shape);
  *   row, bad uniform) cannot be seen without a device sync; they set the
  *   SV_STATUS_* bits of that sequence and make its accepted_len and
  *   out_tokens -1.
+ * Execution: one streaming kernel (every logit read once; per-tile statistics
+ *   and candidates, per-group merges, per-sequence assembly), then in sampling
+ *   mode a draw kernel (residual or bonus draw).  Inside the streaming kernel a
+ *   workgroup only ever waits for workgroups of lower index, with a time bound.
  * The library allocates no memory and keeps no per-call state; it is safe to
  * call from several host threads with separate workspaces.
  */
