@@ -1,19 +1,20 @@
 // spec_verify.hip -- speculative-sampling verification for gfx950 (MI355X).
 //
-// Two launches.
+// Two launches: sv_verify, one workgroup per (group, tile), streams the logits
+// and assembles every sequence; in sampling mode sv_draw, one workgroup per
+// (sequence, tile), then draws the residual or bonus token.
 //
-//  sv_verify  one workgroup per (group, tile).  A group is, for i < k, the pair
-//             (target row i, draft row i) of a sequence and, for i == k, target
-//             row k alone; in greedy mode every group is one target row.  Tiles
-//             are fixed 16 KB slices of a row (8192 bf16 or 4096 fp32 entries).
-//             Each workgroup streams its tile(s) once with 128-bit loads and
-//             publishes a tile record:
+//  sv_verify  A group is, for i < k, the pair (target row i, draft row i) of a
+//             sequence and, for i == k, target row k alone; in greedy mode every
+//             group is one target row.  Tiles are fixed 16 KB slices of a row
+//             (8192 bf16 or 4096 fp32 entries).  Each workgroup streams its
+//             tile(s) once with 128-bit loads and publishes a tile record:
 //               - max and sum of exp2((x - max) * log2(e)/T) of each row part
-//                 (fp32 exp and per-thread fp32 sums, fp64 above the thread);
-//               - 8 of the tile's largest lane maxima (a lane owns 32 bf16 or
-//                 16 fp32 elements);
-//             and, as top-32 candidates, the elements at or above the 16-bit
-//             key bucket of the 8th largest lane maximum.
+//                 (fp32 exp and per-thread fp32 sums, fp64 above the wave);
+//               - 8 lane maxima of distinct lanes (a lane owns 32 bf16 or 16
+//                 fp32 elements), the two largest of each wave;
+//             and, as top-32 candidates, the elements at or above the smallest
+//             of those 8.
 //             The last tile of a group (dispatched after the others) waits for
 //             the others' records and merges the group: row max and normaliser
 //             in tile order, the acceptance decision, and the top-32.  The 32nd
@@ -21,20 +22,21 @@
 //             element from below; candidates at or above it are ranked, and a
 //             tile whose candidate threshold lies above the bound (it may hold
 //             further elements above it) is rescanned, as is a tile whose
-//             candidates overflowed their slots.  The merge of row k also
-//             publishes the tile masses of p_k.
+//             candidates overflowed their slots.
 //             The merge of row k (dispatched after rows 0..k-1) waits for the
 //             sequence's other groups and assembles it: the first rejection j
-//             (greedy: the first draft that differs from the argmax) and the
-//             tokens, except the one to draw.
-//  sv_draw    sampling only, one workgroup per (sequence, tile).  After a
-//             rejection at j every tile of pair row j publishes its residual
-//             mass max(0, p - q); the last one draws by inverse CDF over the tile
-//             masses in tile order and rescans the crossing tile.  After k
-//             acceptances one workgroup draws from p_k over the published masses.
+//             (greedy: the first draft that differs from the argmax), the
+//             tokens, and the position and normalisers of the token to draw.
+//  sv_draw    Each workgroup of a sequence publishes one tile's total mass of
+//             the drawing row: the residual max(0, p - q) of pair row j after a
+//             rejection, p of row k after k acceptances.  Once all tiles of the
+//             row are in, every workgroup finds the crossing tile of u * R over
+//             the totals in tile order, and the one that holds it draws the
+//             token from its registers.
 //
-// In sv_verify, waiting only ever happens on workgroups with a lower index,
-// which the hardware dispatches first, and every wait is bounded in time: a wait that
+// In sv_verify a workgroup only ever waits for workgroups of a lower index,
+// which the hardware dispatches first; in sv_draw for the other workgroups of
+// its sequence, dispatched with it.  Every wait is bounded in time: a wait that
 // gives up sets the fault word (reported as SV_STATUS_SYNC_TIMEOUT) and the
 // kernel still finishes.  Data moves between workgroups through the workspace
 // with device-scope write-through stores and device-scope loads, ordered by
@@ -68,6 +70,8 @@ constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
 constexpr float NEG_INF = -__builtin_inff();
 constexpr uint64_t SPIN_TICKS = 20000000;          // bounded waits give up after 0.2 s (100 MHz clock)
+constexpr int CTR = 64;                            // int32 per counter: each on its own 256 bytes, so
+                                                   // polling one never contends with another
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -104,13 +108,12 @@ struct GroupRec {
   int32_t pad;
 };
 
-// Handed from sv_verify to sv_draw per sequence (valid == 1: a token to draw).
+// Handed from the sequence assembly to the draw workgroups.
 struct SeqRec {
   double s_t, s_d;         // normalisers of the drawing row's target / draft part
   float m_t, m_d;
-  int32_t j, valid;        // drawing position, and whether sv_draw has work
+  int32_t j, valid;        // drawing position (residual for j < k, bonus for j == k); 1: a token to draw
   double u;                // the uniform of the draw
-  int32_t resid, pad;      // 1: residual of the pair row j; 0: target row k
 };
 
 struct Params {
@@ -121,14 +124,13 @@ struct Params {
   int32_t *accepted_len, *out_tokens, *topk_idx, *status;
   float *topk_val, *lse_t, *lse_d, *p_tok, *q_tok;
   int32_t *fault;                      // bit 1: a wait gave up; bit 2: workspace not zero-filled
-  int32_t *garrive, *sarrive, *darrive;
+  int32_t *garrive, *sarrive, *dpub, *ddone;    // counters, CTR int32 apart
   TileRec *recs;
   GroupRec *grec;
   SeqRec *srec;
   uint64_t *cand;                      // [group][tile][SLOTS] candidate keys, 0 = empty
   int32_t *ovf;                        // [group][tile] 1: more candidates than SLOTS
-  double *rsum;                        // [sequence][tile] residual masses of the drawing row
-  double *psum;                        // [sequence][tile] target masses of row k
+  double *dtot;                        // [sequence][tile][2] drawing-row tile totals: residual, p
   int32_t B, k, V, nT;
   float T, sc;                         // sc = log2(e) / T
   double scd;
@@ -145,7 +147,6 @@ struct Smem {
     } fb;
   };
   uint32_t w8[LIST];                   // stream: each wave's two largest lane maxima
-  double tot[MAX_TILES];               // draw: tile masses in tile order
   float f[4][NWAVE];
   int32_t i[4][NWAVE];
   double d[4][NWAVE];
@@ -310,7 +311,7 @@ __device__ __forceinline__ int wait_at_least(const int32_t *p, int target, int32
       atomicOr(fault, 1);
       break;
     }
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(8);
     v = ld_dev(p);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -604,141 +605,6 @@ __device__ __forceinline__ void topk_exact(const char *row, int V, float *oval, 
   __syncthreads();
 }
 
-// Inverse-CDF draw inside one tile: the first element (ascending index) of
-// positive mass whose cumulative mass prefix + (scan base + running fp32 sum)
-// exceeds tau; if rounding leaves none, the tile's last positive-mass element
-// (-1 when the tile has none).  The masses are recomputed exactly as when the
-// tile's total was published.  The running sum never decreases inside a
-// vector, so each thread recomputes only its first vector whose end exceeds
-// tau.
-template <int DT>
-__device__ __forceinline__ int tile_draw(const Params &P, const char *trow, const char *drow, int c, bool resid,
-                                         float m_t, double s_t, float m_d, double s_d, double prefix, double tau,
-                                         Smem &sm) {
-  constexpr int W = Fmt<DT>::W;
-  u32x4 rt[NSEG], rd[NSEG];
-  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
-  if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
-  else
-#pragma unroll
-    for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
-  const float mt = thread_max<DT>(rt);
-  const float md = resid ? thread_max<DT>(rd) : NEG_INF;
-  const float at = prob_scale(mt, m_t, s_t, P.sc);
-  const float ad = resid ? prob_scale(md, m_d, s_d, P.sc) : 0.f;
-  float seg[NSEG];
-  seg_masses<DT>(rt, rd, resid, mt, md, at, ad, P.sc, seg);
-  double base[NSEG];
-  tile_scan(seg, base, sm);
-  int sel = -1;
-  double bsel = 0.0;
-  u32x4 vt = rt[0], vd = rd[0];
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s)
-    if (sel < 0 && prefix + (base[s] + (double)seg[s]) > tau) { sel = s; bsel = base[s]; vt = rt[s]; vd = rd[s]; }
-  int first = 0x7fffffff;
-  if (sel >= 0) {
-    float a = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mval = elem_mass<DT>(vt, vd, w, resid, mt, md, at, ad, P.sc);
-      a += mval;
-      if (first == 0x7fffffff && mval > 0.f && prefix + (bsel + (double)a) > tau) first = tpos<DT>(sel, w);
-    }
-  }
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  first = wave_min_i(first);
-  if (lane == 0) sm.i[2][wid] = first;
-  __syncthreads();
-  int f = sm.i[2][0];
-  for (int w = 1; w < NWAVE; ++w) f = sm.i[2][w] < f ? sm.i[2][w] : f;
-  __syncthreads();
-  if (f != 0x7fffffff) return c * Fmt<DT>::TILE + f;
-  // no crossing inside the tile (rounding): its last positive-mass element,
-  // in each thread's last vector of positive mass
-  int lsel = -1;
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s)
-    if (seg[s] > 0.f) { lsel = s; vt = rt[s]; vd = rd[s]; }
-  int lastpos = -1;
-  if (lsel >= 0) {
-#pragma unroll
-    for (int w = 0; w < W; ++w)
-      if (elem_mass<DT>(vt, vd, w, resid, mt, md, at, ad, P.sc) > 0.f) lastpos = tpos<DT>(lsel, w);
-  }
-  lastpos = wave_max_i(lastpos);
-  if (lane == 0) sm.i[3][wid] = lastpos;
-  __syncthreads();
-  int l = sm.i[3][0];
-  for (int w = 1; w < NWAVE; ++w) l = sm.i[3][w] > l ? sm.i[3][w] : l;
-  __syncthreads();
-  return l < 0 ? -1 : c * Fmt<DT>::TILE + l;
-}
-
-// Total target mass p of one tile (the arithmetic of tile_draw without a draft row).
-template <int DT>
-__device__ __forceinline__ double tile_mass_p(const Params &P, const char *trow, int c, float m_t, double s_t, Smem &sm) {
-  u32x4 rt[NSEG];
-  load_tile<DT>(trow, c, P.V, P.t_vec, rt);
-  const float mt = thread_max<DT>(rt);
-  const float at = prob_scale(mt, m_t, s_t, P.sc);
-  float seg[NSEG];
-  seg_masses<DT>(rt, rt, false, mt, NEG_INF, at, 0.f, P.sc, seg);
-  double base[NSEG];
-  return tile_scan(seg, base, sm);
-}
-
-// The crossing tile of tau = u * R over the tile masses in sm.tot (tile order,
-// R their sum): sm.bc[2] = the first tile whose cumulative mass exceeds tau (-1
-// if none), sm.dbc[0] = the mass before it, sm.dbc[1] = tau.  Run by wave 0.
-__device__ __forceinline__ void locate_tile(int nT, double u, Smem &sm) {
-  const int lane = threadIdx.x & 63;
-  const double cum = wave_scan_d(lane < nT ? sm.tot[lane] : 0.0);
-  const double tau = u * readlane_d(cum, 63);
-  const uint64_t h = __ballot(lane < nT && cum > tau);
-  const int cs = h ? __builtin_ctzll(h) : -1;
-  const double before = cs > 0 ? readlane_d(cum, cs - 1) : 0.0;
-  if (lane == 0) { sm.bc[2] = cs; sm.dbc[0] = before; sm.dbc[1] = tau; }
-}
-
-// Inverse-CDF draw of one token over sm.tot (tile masses of a row in tile
-// order): the crossing tile, then the element inside it.  A residual with no
-// mass left (only through rounding) falls back to p of the same row with the
-// same uniform.  Every thread of the workgroup calls it; returns the token.
-template <int DT>
-__device__ __forceinline__ int draw_row(const Params &P, const char *trow, const char *drow, bool resid, float m_t, double s_t,
-                        float m_d, double s_d, double u, Smem &sm) {
-  const int tid = threadIdx.x, wid = tid >> 6, nT = P.nT;
-  __syncthreads();
-  if (wid == 0) locate_tile(nT, u, sm);
-  __syncthreads();
-  bool use_p = false;
-  if (sm.bc[2] < 0 && resid) {
-    use_p = true;
-    for (int cc = 0; cc < nT; ++cc) {
-      const double m = tile_mass_p<DT>(P, trow, cc, m_t, s_t, sm);
-      if (tid == 0) sm.tot[cc] = m;
-    }
-    __syncthreads();
-    if (wid == 0) locate_tile(nT, u, sm);
-    __syncthreads();
-  }
-  const int cstar = sm.bc[2] >= 0 ? sm.bc[2] : nT - 1;
-  const double prefix = sm.dbc[0], tau = sm.dbc[1];
-  __syncthreads();
-  const bool rmode = resid && !use_p;
-  // the crossing tile; should its recomputed masses all round to zero, the
-  // last positive-mass element before it
-  int token = -1;
-  double pre = prefix, ta = tau;
-  for (int cc = cstar; token < 0 && cc >= 0; --cc) {
-    token = tile_draw<DT>(P, trow, drow, cc, rmode, m_t, s_t, m_d, s_d, pre, ta, sm);
-    pre = 0.0;
-    ta = __builtin_inf();
-  }
-  return token;
-}
-
 struct Geo {
   int g, c, b, i;
   bool pair;
@@ -823,9 +689,7 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
   zero_recs(P.grec + (int64_t)b * K1, K1);
   if (!GREEDY && !st && tid == 0) {
     SeqRec sr;
-    sr.s_t = s_t; sr.s_d = s_d; sr.m_t = m_t; sr.m_d = m_d;
-    sr.j = j; sr.valid = 1; sr.u = u;
-    sr.resid = j < k ? 1 : 0; sr.pad = 0;
+    sr.s_t = s_t; sr.s_d = s_d; sr.m_t = m_t; sr.m_d = m_d; sr.j = j; sr.valid = 1; sr.u = u;
     st_rec(P.srec + b, sr);            // read by sv_draw after this launch
   }
 }
@@ -918,8 +782,6 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         if (dst) dst[(int64_t)b * k + i] = (float)pv;
         if (lane == 1 && P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)M_d / (double)P.T + lg);
       }
-      // row k: the tile masses of p_k, for a bonus draw
-      if (i == k && own) st_dev(P.psum + (int64_t)b * nT + lane, rescale(ts_t, tm_t, M_t, P.sc) / S_t);
     }
 
     // the row bound rb: the 32nd largest of the tiles' lane maxima on 16-bit
@@ -1014,7 +876,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   // the group record is out: announce it, then clear the group's workspace
   // (nothing in this launch reads it again)
   block_stores_done();
-  if (i != k && tid == 0) add_dev_noret(P.sarrive + b, 1);
+  if (i != k && tid == 0) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
 #pragma unroll
   for (int q = 0; q < KEYS_PT; ++q) {
     const int a = tid + q * TPB;
@@ -1028,9 +890,9 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   if (i != k) return;
   // row k is the sequence's last group: wait for the others, then assemble
   if (tid == 0) {
-    const int v = wait_at_least(P.sarrive + b, k, P.fault);
+    const int v = wait_at_least(P.sarrive + (int64_t)b * CTR, k, P.fault);
     if (v > k) atomicOr(P.fault, 2);                                 // workspace not zero-filled
-    st_dev(P.sarrive + b, 0);
+    st_dev(P.sarrive + (int64_t)b * CTR, 0);
   }
   __syncthreads();
   seq_finish<DT, GREEDY>(P, b, sm);
@@ -1079,6 +941,16 @@ __device__ __forceinline__ void wave_stats(const Elems<DT> &e, float mt, float s
   if (__ballot(bad)) flags = __ballot(bad && has_nan_of<DT>(e)) ? SV_STATUS_NAN : SV_STATUS_POSINF;
   // exp2(x*sc - ref*sc) = exp2(x*sc - chi) * exp2(-clo), |clo| <= ulp(chi) / 2
   ws = (double)wave_sum_f(st) * (1.0 - (double)clo * 0.69314718055994531);
+}
+
+// Mass of element w of a vector: max(0, p - q) in residual mode, else p.
+template <int DT>
+__device__ __forceinline__ float draw_mass(const u32x4 &vt, const u32x4 &vd, int w, bool rmode, float mt, float md,
+                                           float at, float ad, float sc) {
+  const float p = scaled_exp(unpack<DT>(vt, w), mt, sc) * at;
+  if (!rmode) return p;
+  const float r = p - scaled_exp(unpack<DT>(vd, w), md, sc) * ad;
+  return r > 0.f ? r : 0.f;
 }
 
 template <int DT, bool GREEDY>
@@ -1207,76 +1079,159 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
   }
   block_stores_done();
   if (c != P.nT - 1) {                                   // not the group's last tile: announce and leave
-    if (tid == 0) add_dev_noret(P.garrive + G.g, 1);
+    if (tid == 0) add_dev_noret(P.garrive + (int64_t)G.g * CTR, 1);
     return;
   }
   // the group's last tile: wait for the other tiles, then merge
   if (tid == 0) {
-    const int v = wait_at_least(P.garrive + G.g, P.nT - 1, P.fault);
+    const int v = wait_at_least(P.garrive + (int64_t)G.g * CTR, P.nT - 1, P.fault);
     if (v > P.nT - 1) atomicOr(P.fault, 2);                          // workspace not zero-filled
-    st_dev(P.garrive + G.g, 0);
+    st_dev(P.garrive + (int64_t)G.g * CTR, 0);
   }
   __syncthreads();
   group_finish<DT, GREEDY>(P, G, xtok, sm);
 }
 
-// Draw workgroup (b, c).  Residual (rejection at j < k): publish tile c's
-// residual mass of pair row j; the last of the sequence's workgroups draws.
-// Bonus (k acceptances): workgroup 0 draws from p_k over the tile masses the
-// merge of row k published.  Every sequence's published masses are cleared.
+// Draw workgroup (b, c).  If sequence b has a token to draw at j, publishes tile c's total mass of the drawing row (the
+// residual max(0, p_j - q_j) for j < k, p_k for j == k), waits for the row's
+// other tiles, finds the crossing tile of tau = u * R over the totals in tile
+// order, and if it holds that tile draws the first positive-mass element whose
+// cumulative mass exceeds tau (the tile's last positive-mass element should
+// rounding leave none).  A residual with no mass left (only through rounding)
+// is replaced by p_j in a second round.  Cumulative masses are the fixed-order
+// fp64 scan of fp32 per-vector sums, the same arithmetic for the totals and for
+// the draw.  The sequence's workgroups are dispatched together, so each waits
+// (bounded) only for workgroups already running.  The last one to finish
+// clears the sequence's state.
 template <int DT>
 __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
   __shared__ Smem sm;
-  const int tid = threadIdx.x;
+  constexpr int W = Fmt<DT>::W;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int nT = P.nT, k = P.k, K1 = k + 1;
   const int b = blockIdx.x / nT, c = blockIdx.x - (blockIdx.x / nT) * nT;
   const SeqRec sr = P.srec[b];
-  // row k's tile masses were published for every sequence; only a bonus draw reads them
-  if ((!sr.valid || sr.resid) && tid == 0) st_dev(P.psum + (int64_t)b * nT + c, 0.0);
   if (!sr.valid) return;
-  const int j = sr.j;
-  const bool resid = sr.resid != 0;
-  if (j < 0 || j > k || (resid && j == k)) {                       // workspace not zero-filled
+  if (sr.j < 0 || sr.j > k) {                                      // workspace not zero-filled
     if (tid == 0) atomicOr(P.fault, 2);
     return;
   }
-  const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
-  const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
-  double *masses;
-  if (!resid) {
-    if (c != 0) return;
-    masses = P.psum + (int64_t)b * nT;
-  } else {
+  double *tot = P.dtot + (int64_t)b * nT * 2;
+  {
+    const int j = sr.j;
+    const bool resid = j < k;
+    const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
+    const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
     u32x4 rt[NSEG], rd[NSEG];
     load_tile<DT>(trow, c, P.V, P.t_vec, rt);
-    load_tile<DT>(drow, c, P.V, P.d_vec, rd);
+    if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
+    else
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
     const float mt = thread_max<DT>(rt);
-    const float md = thread_max<DT>(rd);
+    const float md = resid ? thread_max<DT>(rd) : NEG_INF;
     const float at = prob_scale(mt, sr.m_t, sr.s_t, P.sc);
-    const float ad = prob_scale(md, sr.m_d, sr.s_d, P.sc);
+    const float ad = resid ? prob_scale(md, sr.m_d, sr.s_d, P.sc) : 0.f;
+    bool rmode = resid;
     float seg[NSEG];
-    seg_masses<DT>(rt, rd, true, mt, md, at, ad, P.sc, seg);
     double base[NSEG];
-    const double tot = tile_scan(seg, base, sm);
-    if (tid == 0) st_dev(P.rsum + (int64_t)b * nT + c, tot);
-    const int old = arrive(P.darrive + b, sm);
-    if (old < 0 || old >= nT) { if (tid == 0) atomicOr(P.fault, 2); return; }
-    if (old != nT - 1) return;
-    masses = P.rsum + (int64_t)b * nT;
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      // per-vector sums, their scan over the tile, and the tile total
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rd[s], w, rmode, mt, md, at, ad, P.sc);
+        seg[s] = a;
+      }
+      const double t = tile_scan(seg, base, sm);
+      if (tid == 0) st_dev(tot + 2 * c + round, t);
+      block_stores_done();
+      if (tid == 0) {
+        add_dev_noret(P.dpub + (int64_t)b * CTR, 1);
+        const int v = wait_at_least(P.dpub + (int64_t)b * CTR, (round + 1) * nT, P.fault);
+        if (v > (round + 1) * nT) atomicOr(P.fault, 2);
+      }
+      __syncthreads();
+      // the crossing tile, from the totals in tile order (wave 0)
+      if (wid == 0) {
+        const double cum = wave_scan_d(lane < nT ? ld_dev(tot + 2 * lane + round) : 0.0);
+        const double R = readlane_d(cum, 63);
+        const double tau = sr.u * R;
+        const uint64_t h = __ballot(lane < nT && cum > tau);
+        const int cs = h ? __builtin_ctzll(h) : nT - 1;
+        const double before = cs > 0 ? readlane_d(cum, cs - 1) : 0.0;
+        if (lane == 0) { sm.bc[2] = cs; sm.bc[4] = (rmode && !(R > 0.0)) ? 1 : 0; sm.dbc[0] = before; sm.dbc[1] = tau; }
+      }
+      __syncthreads();
+      if (!sm.bc[4]) break;
+      rmode = false;                   // no residual mass left: draw from p_j
+    }
+    if (sm.bc[2] == c) {
+      // this tile holds the crossing: the first element past tau, recomputed in
+      // each thread's first vector whose running end exceeds it
+      const double prefix = sm.dbc[0], tau = sm.dbc[1];
+      int sel = -1;
+      double bsel = 0.0;
+      u32x4 vt = rt[0], vd = rd[0];
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+        if (sel < 0 && prefix + (base[s] + (double)seg[s]) > tau) { sel = s; bsel = base[s]; vt = rt[s]; vd = rd[s]; }
+      int first = 0x7fffffff;
+      if (sel >= 0) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          const float m = draw_mass<DT>(vt, vd, w, rmode, mt, md, at, ad, P.sc);
+          a += m;
+          if (first == 0x7fffffff && m > 0.f && prefix + (bsel + (double)a) > tau) first = tpos<DT>(sel, w);
+        }
+      }
+      // should rounding leave no element past tau: the last positive-mass one,
+      // in each thread's last vector of positive mass
+      int lsel = -1;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+        if (seg[s] > 0.f) { lsel = s; vt = rt[s]; vd = rd[s]; }
+      int lastpos = -1;
+      if (lsel >= 0) {
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+          if (draw_mass<DT>(vt, vd, w, rmode, mt, md, at, ad, P.sc) > 0.f) lastpos = tpos<DT>(lsel, w);
+      }
+      first = wave_min_i(first);
+      lastpos = wave_max_i(lastpos);
+      if (lane == 0) { sm.i[2][wid] = first; sm.i[3][wid] = lastpos; }
+      __syncthreads();
+      if (tid == 0) {
+        int f = sm.i[2][0], l = sm.i[3][0];
+        for (int w = 1; w < NWAVE; ++w) {
+          f = sm.i[2][w] < f ? sm.i[2][w] : f;
+          l = sm.i[3][w] > l ? sm.i[3][w] : l;
+        }
+        const int pos = f != 0x7fffffff ? f : l;
+        P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+      }
+    }
   }
-  for (int cc = tid; cc < nT; cc += TPB) sm.tot[cc] = ld_dev(masses + cc);
-  const int token = draw_row<DT>(P, trow, drow, resid, sr.m_t, sr.s_t, sr.m_d, sr.s_d, sr.u, sm);
-  if (tid == 0) {
-    P.out_tokens[(int64_t)b * K1 + j] = token;
-    if (resid) st_dev(P.darrive + b, 0);
+  // every draw workgroup of the sequence reports; the last clears its state
+  const int old = arrive(P.ddone + (int64_t)b * CTR, sm);
+  if (old != nT - 1) {
+    if ((old < 0 || old >= nT) && tid == 0) atomicOr(P.fault, 2);
+    return;
   }
-  for (int cc = tid; cc < nT; cc += TPB) st_dev(masses + cc, 0.0);
+  for (int q = tid; q < 2 * nT; q += TPB) st_dev(tot + q, 0.0);
   zero_recs(P.srec + b, 1);
+  if (tid == 0) {
+    st_dev(P.dpub + (int64_t)b * CTR, 0);
+    st_dev(P.ddone + (int64_t)b * CTR, 0);
+  }
 }
 
 // ---------------------------------------------------------------- host side
 struct Layout {
-  size_t fault, garrive, sarrive, darrive, recs, grec, srec, cand, ovf, rsum, psum, total;
+  size_t fault, garrive, sarrive, dpub, ddone, recs, grec, srec, cand, ovf, dtot, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1289,16 +1244,16 @@ Layout layout_for(int B, int k, int V, int dtype) {
   Layout L;
   size_t o = 0;
   L.fault = o;   o = align256(o + sizeof(int32_t));     // fixed header, same offset for every shape
-  L.garrive = o; o = align256(o + groups * sizeof(int32_t));
-  L.sarrive = o; o = align256(o + (size_t)B * sizeof(int32_t));
-  L.darrive = o; o = align256(o + (size_t)B * sizeof(int32_t));
+  L.garrive = o; o = align256(o + groups * CTR * sizeof(int32_t));
+  L.sarrive = o; o = align256(o + (size_t)B * CTR * sizeof(int32_t));
+  L.dpub = o;    o = align256(o + (size_t)B * CTR * sizeof(int32_t));
+  L.ddone = o;   o = align256(o + (size_t)B * CTR * sizeof(int32_t));
   L.recs = o;    o = align256(o + groups * nT * sizeof(TileRec));
   L.grec = o;    o = align256(o + groups * sizeof(GroupRec));
   L.srec = o;    o = align256(o + (size_t)B * sizeof(SeqRec));
   L.cand = o;    o = align256(o + groups * nT * SLOTS * sizeof(uint64_t));
   L.ovf = o;     o = align256(o + groups * nT * sizeof(int32_t));
-  L.rsum = o;    o = align256(o + (size_t)B * nT * sizeof(double));
-  L.psum = o;    o = align256(o + (size_t)B * nT * sizeof(double));
+  L.dtot = o;    o = align256(o + (size_t)B * nT * 2 * sizeof(double));
   L.total = o;
   return L;
 }
@@ -1314,7 +1269,7 @@ hipError_t launch(const Params &P, bool greedy, hipStream_t stream, hipEvent_t e
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipErrorInvalidValue;
   if (greedy) hipLaunchKernelGGL((sv_verify<DT, true>), dim3(items), dim3(TPB), 0, stream, P);
   else hipLaunchKernelGGL((sv_verify<DT, false>), dim3(items), dim3(TPB), 0, stream, P);
-  const hipError_t e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return hipErrorInvalidValue;
   if (greedy) return hipSuccess;
@@ -1390,14 +1345,14 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   P.fault = (int32_t *)(ws + L.fault);
   P.garrive = (int32_t *)(ws + L.garrive);
   P.sarrive = (int32_t *)(ws + L.sarrive);
-  P.darrive = (int32_t *)(ws + L.darrive);
+  P.dpub = (int32_t *)(ws + L.dpub);
+  P.ddone = (int32_t *)(ws + L.ddone);
   P.recs = (TileRec *)(ws + L.recs);
   P.grec = (GroupRec *)(ws + L.grec);
   P.srec = (SeqRec *)(ws + L.srec);
   P.cand = (uint64_t *)(ws + L.cand);
   P.ovf = (int32_t *)(ws + L.ovf);
-  P.rsum = (double *)(ws + L.rsum);
-  P.psum = (double *)(ws + L.psum);
+  P.dtot = (double *)(ws + L.dtot);
   P.B = s.B;
   P.k = s.k;
   P.V = s.V;
