@@ -265,6 +265,15 @@ __device__ __forceinline__ void wave_top2(uint32_t key, uint32_t &k1, uint32_t &
   k1 = readlane(a, 63);
   k2 = readlane(c, 63);
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += (int)dpp<0x111, 0xf, 0xf>(0u, (uint32_t)v);
+  v += (int)dpp<0x112, 0xf, 0xf>(0u, (uint32_t)v);
+  v += (int)dpp<0x114, 0xf, 0xe>(0u, (uint32_t)v);
+  v += (int)dpp<0x118, 0xf, 0xc>(0u, (uint32_t)v);
+  v += (int)dpp<0x142, 0xa, 0xf>(0u, (uint32_t)v);
+  v += (int)dpp<0x143, 0xc, 0xf>(0u, (uint32_t)v);
+  return (int)readlane((uint32_t)v, 63);
+}
 __device__ __forceinline__ float wave_sum_f(float v) {
   v += __uint_as_float(dpp<0x111, 0xf, 0xf>(0u, __float_as_uint(v)));
   v += __uint_as_float(dpp<0x112, 0xf, 0xf>(0u, __float_as_uint(v)));
@@ -694,6 +703,22 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
   }
 }
 
+// 2^a for a <= 0 to about 2e-7 relative: the integer part scales exactly, the
+// fraction in [-1/2, 1/2] goes through the hardware fp32 exp2
+__device__ __forceinline__ double exp2_split(double a) {
+  if (!(a > -1100.0)) return 0.0;
+  const double n = __builtin_rint(a);
+  return __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
+}
+
+// natural log of s > 0 to about 1e-7 absolute: exponent exactly, mantissa in
+// [1/2, 1) through the hardware fp32 log2
+__device__ __forceinline__ double log_split(double s) {
+  int e;
+  const double m = __builtin_frexp(s, &e);
+  return ((double)e + (double)__builtin_amdgcn_logf((float)m)) * 0.6931471805599453;
+}
+
 // Row combine, acceptance decision and top-32 merge of group g (run by its last
 // tile once the others have published), then the sequence's arrival.
 template <int DT, bool GREEDY>
@@ -713,26 +738,27 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     const int a = tid + q * TPB;
     key[q] = a < nslot ? ld_dev(slots + a) : 0ull;
   }
+  // wave 0 takes words 0-3 of tile record `lane` (statistics), wave 1 words
+  // 3-7 (candidate threshold, lane maxima) and the tile's overflow flag
   uint64_t *rsrc = (uint64_t *)(P.recs + (int64_t)g * nT) + lane * 8;
   uint64_t rw[8];
   int32_t ov = 0;
-  const bool own = wid == 0 && lane < nT;
+  const bool own = wid == 0 && lane < nT, own1 = wid == 1 && lane < nT;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) rw[q] = own ? ld_dev(rsrc + q) : 0ull;
-  if (own) ov = ld_dev(P.ovf + (int64_t)g * nT + lane);
+  for (int q = 0; q < 8; ++q) rw[q] = ((own && q <= 3) || (own1 && q >= 3)) ? ld_dev(rsrc + q) : 0ull;
+  if (own1) ov = ld_dev(P.ovf + (int64_t)g * nT + lane);
   float lv = 0.f;                              // lane 0: t_x, lane 1: d_x
   float ui = 0.f;
   if (pair && wid == 0 && lane < 2 && x >= 0 && x < V) lv = load_elem<DT>(lane == 0 ? G.trow : G.drow, x);
   if (pair && tid == 0) ui = P.uniforms[(int64_t)b * (k + 2) + i];
 
-  // ---- wave 0: row statistics, decision, group record, and the row bound
+  // ---- wave 0: row statistics, decision and group record; wave 1: the row bound
   float M_t = NEG_INF;
   int fl = 0;
   if (wid == 0) {
     const float tm_t = __uint_as_float((uint32_t)rw[0]), tm_d = __uint_as_float((uint32_t)(rw[0] >> 32));
     const double ts_t = __builtin_bit_cast(double, rw[1]), ts_d = __builtin_bit_cast(double, rw[2]);
     int fa = own ? (int)((uint32_t)rw[3] & 0xffu) : 0, fd = own ? (int)(((uint32_t)rw[3] >> 8) & 0xffu) : 0;
-    const uint32_t kthr = (uint32_t)(rw[3] >> 32);
     M_t = wave_max_f(own ? tm_t : NEG_INF);
     const float M_d = pair ? wave_max_f(own ? tm_d : NEG_INF) : NEG_INF;
     fa = wave_or(fa);
@@ -760,7 +786,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         } else if (!fl) {
           const double mm = lane == 0 ? (double)M_t : (double)M_d;
           const double ss = lane == 0 ? S_t : S_d;
-          pv = exp2(((double)lv - mm) * P.scd) / ss;
+          pv = exp2_split(((double)lv - mm) * P.scd) / ss;
           const double p = readlane_d(pv, 0), q = readlane_d(pv, 1);
           const double ratio = q > 0.0 ? p / q : (p > 0.0 ? __builtin_inf() : 0.0);
           const double a = ratio < 1.0 ? ratio : 1.0;
@@ -769,7 +795,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
           acc = 0;
         }
       }
-      const double lg = log(lane == 0 ? S_t : S_d);
+      const double lg = log_split(lane == 0 ? S_t : S_d);
       if (lane == 0) {
         GroupRec gr;
         gr.s_t = S_t; gr.s_d = S_d; gr.m_t = M_t; gr.m_d = M_d;
@@ -782,10 +808,20 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         if (dst) dst[(int64_t)b * k + i] = (float)pv;
         if (lane == 1 && P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)M_d / (double)P.T + lg);
       }
+      // the group record is out: announce it to the sequence now (the top-32
+      // is not part of it)
+      stores_done();
+      if (lane == 0 && i != k) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
     }
 
+    if (lane == 0) {
+      sm.bc[2] = fa;                           // the target row's own flags decide its top-32
+      sm.bc[6] = -1;
+    }
+  } else if (wid == 1) {
     // the row bound rb: the 32nd largest of the tiles' lane maxima on 16-bit
     // buckets (0 when there are fewer than 32), found bit by bit from the top
+    const uint32_t kthr = (uint32_t)(rw[3] >> 32);
     uint32_t top[LIST];
 #pragma unroll
     for (int q = 0; q < LIST / 2; ++q) {
@@ -797,18 +833,16 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
       const uint32_t c = rb | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int q = 0; q < LIST; ++q) cnt += __popcll(__ballot(top[q] >= c));
-      if (cnt >= TOPK) rb = c;
+      for (int q = 0; q < LIST; ++q) cnt += top[q] >= c ? 1 : 0;
+      if (wave_sum_i(cnt) >= TOPK) rb = c;
     }
     // tiles to rescan: candidates overflowed, or the candidate threshold lies
     // above the bound (elements between the two were not published)
-    const uint64_t rs = __ballot(own && (ov != 0 || kthr > (rb | Fmt<DT>::LOW)));
+    const uint64_t rs = __ballot(own1 && (ov != 0 || kthr > (rb | Fmt<DT>::LOW)));
     if (lane == 0) {
       sm.rescan = rs;
       sm.bc[0] = 0;
       sm.bc[1] = (int)rb;
-      sm.bc[2] = fa;                           // the target row's own flags decide its top-32
-      sm.bc[6] = -1;
     }
   }
   __syncthreads();
@@ -876,7 +910,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   // the group record is out: announce it, then clear the group's workspace
   // (nothing in this launch reads it again)
   block_stores_done();
-  if (i != k && tid == 0) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
+  if (GREEDY && i != k && tid == 0) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
 #pragma unroll
   for (int q = 0; q < KEYS_PT; ++q) {
     const int a = tid + q * TPB;
@@ -885,8 +919,8 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   if (own) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) st_dev(rsrc + q, (uint64_t)0);
-    if (ov) st_dev(P.ovf + (int64_t)g * nT + lane, 0);
   }
+  if (ov) st_dev(P.ovf + (int64_t)g * nT + lane, 0);
   if (i != k) return;
   // row k is the sequence's last group: wait for the others, then assemble
   if (tid == 0) {
@@ -943,13 +977,15 @@ __device__ __forceinline__ void wave_stats(const Elems<DT> &e, float mt, float s
   ws = (double)wave_sum_f(st) * (1.0 - (double)clo * 0.69314718055994531);
 }
 
-// Mass of element w of a vector: max(0, p - q) in residual mode, else p.
+// Mass of element w of a vector: max(0, p - q) in residual mode, else p, with
+// p = exp2(x * sc - ot) and q = exp2(y * sc - od), where ot = m_t * sc +
+// log2(s_t) folds the row max and normaliser into one offset (od likewise).
 template <int DT>
-__device__ __forceinline__ float draw_mass(const u32x4 &vt, const u32x4 &vd, int w, bool rmode, float mt, float md,
-                                           float at, float ad, float sc) {
-  const float p = scaled_exp(unpack<DT>(vt, w), mt, sc) * at;
+__device__ __forceinline__ float draw_mass(const u32x4 &vt, const u32x4 &vd, int w, bool rmode, float ot, float od,
+                                           float sc) {
+  const float p = __builtin_amdgcn_exp2f(fmaf(unpack<DT>(vt, w), sc, -ot));
   if (!rmode) return p;
-  const float r = p - scaled_exp(unpack<DT>(vd, w), md, sc) * ad;
+  const float r = p - __builtin_amdgcn_exp2f(fmaf(unpack<DT>(vd, w), sc, -od));
   return r > 0.f ? r : 0.f;
 }
 
@@ -1128,10 +1164,8 @@ __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
     else
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
-    const float mt = thread_max<DT>(rt);
-    const float md = resid ? thread_max<DT>(rd) : NEG_INF;
-    const float at = prob_scale(mt, sr.m_t, sr.s_t, P.sc);
-    const float ad = resid ? prob_scale(md, sr.m_d, sr.s_d, P.sc) : 0.f;
+    const float ot = (float)((double)sr.m_t * P.scd + log2(sr.s_t));
+    const float od = resid ? (float)((double)sr.m_d * P.scd + log2(sr.s_d)) : 0.f;
     bool rmode = resid;
     float seg[NSEG];
     double base[NSEG];
@@ -1142,7 +1176,7 @@ __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
       for (int s = 0; s < NSEG; ++s) {
         float a = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rd[s], w, rmode, mt, md, at, ad, P.sc);
+        for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rd[s], w, rmode, ot, od, P.sc);
         seg[s] = a;
       }
       const double t = tile_scan(seg, base, sm);
@@ -1183,7 +1217,7 @@ __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
         float a = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-          const float m = draw_mass<DT>(vt, vd, w, rmode, mt, md, at, ad, P.sc);
+          const float m = draw_mass<DT>(vt, vd, w, rmode, ot, od, P.sc);
           a += m;
           if (first == 0x7fffffff && m > 0.f && prefix + (bsel + (double)a) > tau) first = tpos<DT>(sel, w);
         }
@@ -1198,7 +1232,7 @@ __global__ __launch_bounds__(TPB) void sv_draw(Params P) {
       if (lsel >= 0) {
 #pragma unroll
         for (int w = 0; w < W; ++w)
-          if (draw_mass<DT>(vt, vd, w, rmode, mt, md, at, ad, P.sc) > 0.f) lastpos = tpos<DT>(lsel, w);
+          if (draw_mass<DT>(vt, vd, w, rmode, ot, od, P.sc) > 0.f) lastpos = tpos<DT>(lsel, w);
       }
       first = wave_min_i(first);
       lastpos = wave_max_i(lastpos);
