@@ -110,11 +110,12 @@ struct GroupRec {
 
 // Handed from the sequence assembly to the draw workgroups.
 struct SeqRec {
-  double s_t, s_d;         // normalisers of the drawing row's target / draft part
-  float m_t, m_d;
-  int32_t j, valid;        // drawing position (residual for j < k, bonus for j == k); 1: a token to draw
+  float ot, od;            // drawing row offsets m * log2(e)/T + log2(s) of its target / draft part
+  int32_t j;               // drawing position: residual for j < k, bonus for j == k
+  int32_t state;           // 0: not assembled yet; 1: a token to draw; 2: none (data error)
   double u;                // the uniform of the draw
 };
+constexpr int SREC_STRIDE = 256;       // bytes per sequence record: its pollers share no line
 
 struct Params {
   const char *target, *draft;
@@ -132,6 +133,7 @@ struct Params {
   int32_t *ovf;                        // [group][tile] 1: more candidates than SLOTS
   double *dtot;                        // [sequence][tile][2] drawing-row tile totals: residual, p
   int32_t B, k, V, nT;
+  int32_t items;                       // streaming workgroups: B * (k + 1) * nT
   float T, sc;                         // sc = log2(e) / T
   double scd;
   int32_t t_vec, d_vec;                // rows 16-byte aligned
@@ -382,14 +384,22 @@ template <int DT> __device__ __forceinline__ int tpos(int s, int w) {
   return s * (TPB * Fmt<DT>::W) + (int)threadIdx.x * Fmt<DT>::W + w;
 }
 
+// tile-local position of element w of this thread's vector s when each thread
+// owns NSEG consecutive vectors (the draw's order)
+template <int DT> __device__ __forceinline__ int dpos(int s, int w) {
+  return ((int)threadIdx.x * NSEG + s) * Fmt<DT>::W + w;
+}
+
 // Stream one tile of a row into registers; entries past V read as -inf.
-template <int DT>
+// Vector s of a thread sits at tpos (vectors interleaved over the threads) or,
+// with TM, at dpos (each thread's vectors consecutive).
+template <int DT, bool TM = false>
 __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool vec, u32x4 (&r)[NSEG]) {
   constexpr int E = Fmt<DT>::E, W = Fmt<DT>::W;
   const int64_t c0 = (int64_t)c * Fmt<DT>::TILE;
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
-    const int64_t e0 = c0 + s * (TPB * W) + (int64_t)threadIdx.x * W;
+    const int64_t e0 = c0 + (TM ? dpos<DT>(s, 0) : tpos<DT>(s, 0));
     if (vec && e0 + W <= V) {
       r[s] = __builtin_nontemporal_load((const u32x4 *)(row + e0 * E));
     } else {
@@ -483,33 +493,23 @@ __device__ __forceinline__ void seg_masses(const u32x4 (&rt)[NSEG], const u32x4 
   }
 }
 
-// Exclusive prefix (fp64) of per-thread vector masses over the tile, in the
-// tile's element order (vector-major, then thread).  base[s] receives the mass
-// of all tile elements before this thread's vector s; returns the tile total.
-// Fixed association: identical bits wherever it is evaluated.
-__device__ __forceinline__ double tile_scan(const float (&seg)[NSEG], double (&base)[NSEG], Smem &sm) {
+// Exclusive prefix (fp64) of one value per thread over the workgroup, in
+// thread order: excl receives the sum over the threads before this one; returns
+// the total.  Fixed association: identical bits wherever it is evaluated.
+__device__ __forceinline__ double block_scan_d(double x, double &excl, Smem &sm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  double prev[NSEG];
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    const double inc = wave_scan_d((double)seg[s]);
-    prev[s] = wave_prev_d(inc);
-    if (lane == 63) sm.d[s][wid] = inc;
-  }
+  const double inc = wave_scan_d(x);
+  const double prev = wave_prev_d(inc);
+  if (lane == 63) sm.d[0][wid] = inc;
   __syncthreads();
-  double acc = 0.0;
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    double off = 0.0, tot = 0.0;
-    for (int w = 0; w < NWAVE; ++w) {
-      if (w < wid) off += sm.d[s][w];
-      tot += sm.d[s][w];
-    }
-    base[s] = acc + (off + prev[s]);
-    acc = acc + tot;
+  double off = 0.0, tot = 0.0;
+  for (int w = 0; w < NWAVE; ++w) {
+    if (w < wid) off += sm.d[0][w];
+    tot += sm.d[0][w];
   }
+  excl = off + prev;
   __syncthreads();
-  return acc;
+  return tot;
 }
 
 // Block-wide OR and MIN.
@@ -696,10 +696,19 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
     if (st || i != j || GREEDY) P.out_tokens[(int64_t)b * K1 + i] = v;
   }
   zero_recs(P.grec + (int64_t)b * K1, K1);
-  if (!GREEDY && !st && tid == 0) {
-    SeqRec sr;
-    sr.s_t = s_t; sr.s_d = s_d; sr.m_t = m_t; sr.m_d = m_d; sr.j = j; sr.valid = 1; sr.u = u;
-    st_rec(P.srec + b, sr);            // read by sv_draw after this launch
+  if (!GREEDY && tid == 0) {
+    // the draw workgroups wait for the state word: the record first, then it
+    SeqRec sr = {};
+    if (!st) {
+      sr.ot = (float)((double)m_t * P.scd + log2(s_t));
+      sr.od = j < k ? (float)((double)m_d * P.scd + log2(s_d)) : 0.f;
+      sr.j = j;
+      sr.u = u;
+    }
+    SeqRec *rec = (SeqRec *)((char *)P.srec + (int64_t)b * SREC_STRIDE);
+    st_rec(rec, sr);
+    stores_done();
+    st_dev(&rec->state, st ? 2 : 1);
   }
 }
 
@@ -989,6 +998,150 @@ __device__ __forceinline__ float draw_mass(const u32x4 &vt, const u32x4 &vd, int
   return r > 0.f ? r : 0.f;
 }
 
+// Draw workgroup (b, c), dispatched after every streaming workgroup.  It waits
+// (bounded) for sequence b's assembly; if the sequence has a token to draw at
+// j, it publishes tile c's total mass of the drawing row (the residual
+// max(0, p_j - q_j) for j < k, p_k for j == k), waits for the row's other
+// tiles, finds the crossing tile of tau = u * R over the totals in tile order,
+// and if it holds that tile draws the first positive-mass element whose
+// cumulative mass exceeds tau (the tile's last positive-mass element should
+// rounding leave none).  A residual with no mass left (only through rounding)
+// is replaced by p_j in a second round.  Cumulative masses are the fixed-order
+// fp64 scan of fp32 per-vector sums, the same arithmetic for the totals and for
+// the draw.  A sequence's draw workgroups are consecutive, so each waits only
+// for workgroups dispatched with it or before it.  The last one to finish
+// clears the sequence's state.
+template <int DT>
+__device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &sm) {
+  constexpr int W = Fmt<DT>::W;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nT = P.nT, k = P.k, K1 = k + 1;
+  SeqRec *rec = (SeqRec *)((char *)P.srec + (int64_t)b * SREC_STRIDE);
+  if (tid == 0) {
+    const int v = wait_at_least(&rec->state, 1, P.fault);
+    int j = -1;
+    if (v == 1) {
+      const SeqRec r = ld_rec(rec);
+      j = r.j;
+      if (j < 0 || j > k) { atomicOr(P.fault, 2); j = -1; }  // workspace not zero-filled
+      sm.f[2][0] = r.ot;
+      sm.f[2][1] = r.od;
+      sm.dbc[2] = r.u;
+    } else if (v > 2) {
+      atomicOr(P.fault, 2);
+    }
+    sm.bc[3] = j;
+  }
+  __syncthreads();
+  const int j = sm.bc[3];
+  double *tot = P.dtot + (int64_t)b * nT * 2;
+  if (j >= 0) {
+    const bool resid = j < k;
+    const float ot = sm.f[2][0], od = sm.f[2][1];
+    const double u = sm.dbc[2];
+    const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
+    const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
+    u32x4 rt[NSEG], rd[NSEG];
+    load_tile<DT, true>(trow, c, P.V, P.t_vec, rt);
+    if (resid) load_tile<DT, true>(drow, c, P.V, P.d_vec, rd);
+    else
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
+    bool rmode = resid;
+    float mine = 0.f;                  // mass of this thread's elements, summed in order
+    double base = 0.0;                 // mass of the tile's elements before them
+#pragma unroll 1
+    for (int round = 0; round < 2; ++round) {
+      // the thread's sum, its scan over the tile, and the tile total.  The
+      // offsets and data pass through an empty asm so that the compiler
+      // unpacks and computes the masses here, element by element, instead of
+      // hoisting them out of the loop and keeping them live
+      float o1 = ot, o2 = od;
+      asm volatile("" : "+v"(o1), "+v"(o2));
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) asm volatile("" : "+v"(rt[s]), "+v"(rd[s]));
+      float a = 0.f;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+        for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rd[s], w, rmode, o1, o2, P.sc);
+      mine = a;
+      const double t = block_scan_d((double)a, base, sm);
+      if (tid == 0) st_dev(tot + 2 * c + round, t);
+      block_stores_done();
+      if (tid == 0) {
+        add_dev_noret(P.dpub + (int64_t)b * CTR, 1);
+        const int v = wait_at_least(P.dpub + (int64_t)b * CTR, (round + 1) * nT, P.fault);
+        if (v > (round + 1) * nT) atomicOr(P.fault, 2);
+      }
+      __syncthreads();
+      // the crossing tile, from the totals in tile order (wave 0)
+      if (wid == 0) {
+        const double cum = wave_scan_d(lane < nT ? ld_dev(tot + 2 * lane + round) : 0.0);
+        const double R = readlane_d(cum, 63);
+        const double tau = u * R;
+        const uint64_t h = __ballot(lane < nT && cum > tau);
+        const int cs = h ? __builtin_ctzll(h) : nT - 1;
+        const double before = cs > 0 ? readlane_d(cum, cs - 1) : 0.0;
+        if (lane == 0) { sm.bc[2] = cs; sm.bc[4] = (rmode && !(R > 0.0)) ? 1 : 0; sm.dbc[0] = before; sm.dbc[1] = tau; }
+      }
+      __syncthreads();
+      if (!sm.bc[4]) break;
+      rmode = false;                   // no residual mass left: draw from p_j
+    }
+    if (sm.bc[2] == c) {
+      // this tile holds the crossing: the first positive-mass element whose
+      // running total passes tau, and the last positive-mass element should
+      // rounding leave none, each thread walking its elements in order
+      const double prefix = sm.dbc[0], tau = sm.dbc[1];
+      float o1 = ot, o2 = od;
+      asm volatile("" : "+v"(o1), "+v"(o2));
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) asm volatile("" : "+v"(rt[s]), "+v"(rd[s]));
+      int first = 0x7fffffff, lastpos = -1;
+      if (mine > 0.f) {
+        float a = 0.f;
+#pragma unroll
+        for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            const float m = draw_mass<DT>(rt[s], rd[s], w, rmode, o1, o2, P.sc);
+            a += m;
+            if (m > 0.f) {
+              if (first == 0x7fffffff && prefix + (base + (double)a) > tau) first = dpos<DT>(s, w);
+              lastpos = dpos<DT>(s, w);
+            }
+          }
+      }
+      first = wave_min_i(first);
+      lastpos = wave_max_i(lastpos);
+      if (lane == 0) { sm.i[2][wid] = first; sm.i[3][wid] = lastpos; }
+      __syncthreads();
+      if (tid == 0) {
+        int f = sm.i[2][0], l = sm.i[3][0];
+        for (int w = 1; w < NWAVE; ++w) {
+          f = sm.i[2][w] < f ? sm.i[2][w] : f;
+          l = sm.i[3][w] > l ? sm.i[3][w] : l;
+        }
+        const int pos = f != 0x7fffffff ? f : l;
+        P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+      }
+    }
+  }
+  // every draw workgroup of the sequence reports; the last clears its state
+  const int old = arrive(P.ddone + (int64_t)b * CTR, sm);
+  if (old != nT - 1) {
+    if ((old < 0 || old >= nT) && tid == 0) atomicOr(P.fault, 2);
+    return;
+  }
+  for (int q = tid; q < 2 * nT; q += TPB) st_dev(tot + q, 0.0);
+  zero_recs(rec, 1);
+  if (tid == 0) {
+    st_dev(P.dpub + (int64_t)b * CTR, 0);
+    st_dev(P.ddone + (int64_t)b * CTR, 0);
+  }
+}
+
 template <int DT, bool GREEDY>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) void sv_verify(Params P) {
   __shared__ Smem sm;
@@ -996,6 +1149,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int V = P.V;
   const int item = blockIdx.x;
+  if (!GREEDY && item >= P.items) {                      // draw workgroups come last
+    const int d = item - P.items;
+    draw_tile<DT>(P, d / P.nT, d - (d / P.nT) * P.nT, sm);
+    return;
+  }
   const Geo G = geo<DT, GREEDY>(P, item);
   const int c = G.c;
   const bool pair = G.pair;
@@ -1128,141 +1286,6 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
   group_finish<DT, GREEDY>(P, G, xtok, sm);
 }
 
-// Draw workgroup (b, c).  If sequence b has a token to draw at j, publishes tile c's total mass of the drawing row (the
-// residual max(0, p_j - q_j) for j < k, p_k for j == k), waits for the row's
-// other tiles, finds the crossing tile of tau = u * R over the totals in tile
-// order, and if it holds that tile draws the first positive-mass element whose
-// cumulative mass exceeds tau (the tile's last positive-mass element should
-// rounding leave none).  A residual with no mass left (only through rounding)
-// is replaced by p_j in a second round.  Cumulative masses are the fixed-order
-// fp64 scan of fp32 per-vector sums, the same arithmetic for the totals and for
-// the draw.  The sequence's workgroups are dispatched together, so each waits
-// (bounded) only for workgroups already running.  The last one to finish
-// clears the sequence's state.
-template <int DT>
-__global__ __launch_bounds__(TPB) void sv_draw(Params P) {
-  __shared__ Smem sm;
-  constexpr int W = Fmt<DT>::W;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nT = P.nT, k = P.k, K1 = k + 1;
-  const int b = blockIdx.x / nT, c = blockIdx.x - (blockIdx.x / nT) * nT;
-  const SeqRec sr = P.srec[b];
-  if (!sr.valid) return;
-  if (sr.j < 0 || sr.j > k) {                                      // workspace not zero-filled
-    if (tid == 0) atomicOr(P.fault, 2);
-    return;
-  }
-  double *tot = P.dtot + (int64_t)b * nT * 2;
-  {
-    const int j = sr.j;
-    const bool resid = j < k;
-    const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
-    const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
-    u32x4 rt[NSEG], rd[NSEG];
-    load_tile<DT>(trow, c, P.V, P.t_vec, rt);
-    if (resid) load_tile<DT>(drow, c, P.V, P.d_vec, rd);
-    else
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s) rd[s] = rt[s];
-    const float ot = (float)((double)sr.m_t * P.scd + log2(sr.s_t));
-    const float od = resid ? (float)((double)sr.m_d * P.scd + log2(sr.s_d)) : 0.f;
-    bool rmode = resid;
-    float seg[NSEG];
-    double base[NSEG];
-#pragma unroll
-    for (int round = 0; round < 2; ++round) {
-      // per-vector sums, their scan over the tile, and the tile total
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s) {
-        float a = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rd[s], w, rmode, ot, od, P.sc);
-        seg[s] = a;
-      }
-      const double t = tile_scan(seg, base, sm);
-      if (tid == 0) st_dev(tot + 2 * c + round, t);
-      block_stores_done();
-      if (tid == 0) {
-        add_dev_noret(P.dpub + (int64_t)b * CTR, 1);
-        const int v = wait_at_least(P.dpub + (int64_t)b * CTR, (round + 1) * nT, P.fault);
-        if (v > (round + 1) * nT) atomicOr(P.fault, 2);
-      }
-      __syncthreads();
-      // the crossing tile, from the totals in tile order (wave 0)
-      if (wid == 0) {
-        const double cum = wave_scan_d(lane < nT ? ld_dev(tot + 2 * lane + round) : 0.0);
-        const double R = readlane_d(cum, 63);
-        const double tau = sr.u * R;
-        const uint64_t h = __ballot(lane < nT && cum > tau);
-        const int cs = h ? __builtin_ctzll(h) : nT - 1;
-        const double before = cs > 0 ? readlane_d(cum, cs - 1) : 0.0;
-        if (lane == 0) { sm.bc[2] = cs; sm.bc[4] = (rmode && !(R > 0.0)) ? 1 : 0; sm.dbc[0] = before; sm.dbc[1] = tau; }
-      }
-      __syncthreads();
-      if (!sm.bc[4]) break;
-      rmode = false;                   // no residual mass left: draw from p_j
-    }
-    if (sm.bc[2] == c) {
-      // this tile holds the crossing: the first element past tau, recomputed in
-      // each thread's first vector whose running end exceeds it
-      const double prefix = sm.dbc[0], tau = sm.dbc[1];
-      int sel = -1;
-      double bsel = 0.0;
-      u32x4 vt = rt[0], vd = rd[0];
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s)
-        if (sel < 0 && prefix + (base[s] + (double)seg[s]) > tau) { sel = s; bsel = base[s]; vt = rt[s]; vd = rd[s]; }
-      int first = 0x7fffffff;
-      if (sel >= 0) {
-        float a = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          const float m = draw_mass<DT>(vt, vd, w, rmode, ot, od, P.sc);
-          a += m;
-          if (first == 0x7fffffff && m > 0.f && prefix + (bsel + (double)a) > tau) first = tpos<DT>(sel, w);
-        }
-      }
-      // should rounding leave no element past tau: the last positive-mass one,
-      // in each thread's last vector of positive mass
-      int lsel = -1;
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s)
-        if (seg[s] > 0.f) { lsel = s; vt = rt[s]; vd = rd[s]; }
-      int lastpos = -1;
-      if (lsel >= 0) {
-#pragma unroll
-        for (int w = 0; w < W; ++w)
-          if (draw_mass<DT>(vt, vd, w, rmode, ot, od, P.sc) > 0.f) lastpos = tpos<DT>(lsel, w);
-      }
-      first = wave_min_i(first);
-      lastpos = wave_max_i(lastpos);
-      if (lane == 0) { sm.i[2][wid] = first; sm.i[3][wid] = lastpos; }
-      __syncthreads();
-      if (tid == 0) {
-        int f = sm.i[2][0], l = sm.i[3][0];
-        for (int w = 1; w < NWAVE; ++w) {
-          f = sm.i[2][w] < f ? sm.i[2][w] : f;
-          l = sm.i[3][w] > l ? sm.i[3][w] : l;
-        }
-        const int pos = f != 0x7fffffff ? f : l;
-        P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
-      }
-    }
-  }
-  // every draw workgroup of the sequence reports; the last clears its state
-  const int old = arrive(P.ddone + (int64_t)b * CTR, sm);
-  if (old != nT - 1) {
-    if ((old < 0 || old >= nT) && tid == 0) atomicOr(P.fault, 2);
-    return;
-  }
-  for (int q = tid; q < 2 * nT; q += TPB) st_dev(tot + q, 0.0);
-  zero_recs(P.srec + b, 1);
-  if (tid == 0) {
-    st_dev(P.dpub + (int64_t)b * CTR, 0);
-    st_dev(P.ddone + (int64_t)b * CTR, 0);
-  }
-}
-
 // ---------------------------------------------------------------- host side
 struct Layout {
   size_t fault, garrive, sarrive, dpub, ddone, recs, grec, srec, cand, ovf, dtot, total;
@@ -1284,7 +1307,7 @@ Layout layout_for(int B, int k, int V, int dtype) {
   L.ddone = o;   o = align256(o + (size_t)B * CTR * sizeof(int32_t));
   L.recs = o;    o = align256(o + groups * nT * sizeof(TileRec));
   L.grec = o;    o = align256(o + groups * sizeof(GroupRec));
-  L.srec = o;    o = align256(o + (size_t)B * sizeof(SeqRec));
+  L.srec = o;    o = align256(o + (size_t)B * SREC_STRIDE);
   L.cand = o;    o = align256(o + groups * nT * SLOTS * sizeof(uint64_t));
   L.ovf = o;     o = align256(o + groups * nT * sizeof(int32_t));
   L.dtot = o;    o = align256(o + (size_t)B * nT * 2 * sizeof(double));
@@ -1299,16 +1322,15 @@ bool shape_ok(const sv_shape_t *s) {
 
 template <int DT>
 hipError_t launch(const Params &P, bool greedy, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const unsigned items = (unsigned)((int64_t)P.B * (P.k + 1) * P.nT);
+  // streaming workgroups, then (sampling) one draw workgroup per (sequence, tile)
+  const unsigned grid = (unsigned)P.items + (greedy ? 0u : (unsigned)P.B * (unsigned)P.nT);
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipErrorInvalidValue;
-  if (greedy) hipLaunchKernelGGL((sv_verify<DT, true>), dim3(items), dim3(TPB), 0, stream, P);
-  else hipLaunchKernelGGL((sv_verify<DT, false>), dim3(items), dim3(TPB), 0, stream, P);
-  hipError_t e = hipGetLastError();
+  if (greedy) hipLaunchKernelGGL((sv_verify<DT, true>), dim3(grid), dim3(TPB), 0, stream, P);
+  else hipLaunchKernelGGL((sv_verify<DT, false>), dim3(grid), dim3(TPB), 0, stream, P);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return hipErrorInvalidValue;
-  if (greedy) return hipSuccess;
-  hipLaunchKernelGGL((sv_draw<DT>), dim3((unsigned)((int64_t)P.B * P.nT)), dim3(TPB), 0, stream, P);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace
@@ -1348,7 +1370,7 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   const int tile = tile_of(s.dtype);
   const int64_t nT = ((int64_t)s.V + tile - 1) / tile;
   const int64_t items = (int64_t)s.B * (s.k + 1) * nT;
-  if (items > 0x7fffffffLL || (int64_t)s.B * (s.k + 2) > 0x7fffffffLL) return SV_ERR_SHAPE;
+  if (items + (int64_t)s.B * nT > 0x7fffffffLL || (int64_t)s.B * (s.k + 2) > 0x7fffffffLL) return SV_ERR_SHAPE;
   if (!(s.temperature >= 0.f) || s.temperature == __builtin_inff()) return SV_ERR_TEMPERATURE;
   const bool greedy = s.temperature == 0.f;
   if (s.B == 0) return SV_OK;
@@ -1391,6 +1413,7 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   P.k = s.k;
   P.V = s.V;
   P.nT = (int32_t)nT;
+  P.items = (int32_t)items;
   P.T = greedy ? 0.f : s.temperature;
   P.scd = greedy ? 0.0 : 1.4426950408889634 / (double)s.temperature;
   P.sc = (float)P.scd;
