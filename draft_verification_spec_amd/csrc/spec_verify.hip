@@ -858,6 +858,17 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   const uint32_t rb = (uint32_t)sm.bc[1];
   const bool nanrow = (sm.bc[2] & SV_STATUS_NAN) != 0;
   const uint64_t rs = sm.rescan;
+  if (!GREEDY && i == k) {
+    // sampling: the sequence's assembly needs no top-32, so row k assembles
+    // the sequence (once the other groups have announced) before its own merge
+    if (tid == 0) {
+      const int v = wait_at_least(P.sarrive + (int64_t)b * CTR, k, P.fault);
+      if (v > k) atomicOr(P.fault, 2);                               // workspace not zero-filled
+      st_dev(P.sarrive + (int64_t)b * CTR, 0);
+    }
+    __syncthreads();
+    seq_finish<DT, GREEDY>(P, b, sm);
+  }
 
   // ---- candidates at or above the bound: slots of complete tiles, then rescans
   if (!nanrow) {
@@ -930,7 +941,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     for (int q = 0; q < 8; ++q) st_dev(rsrc + q, (uint64_t)0);
   }
   if (ov) st_dev(P.ovf + (int64_t)g * nT + lane, 0);
-  if (i != k) return;
+  if (!GREEDY || i != k) return;
   // row k is the sequence's last group: wait for the others, then assemble
   if (tid == 0) {
     const int v = wait_at_least(P.sarrive + (int64_t)b * CTR, k, P.fault);
