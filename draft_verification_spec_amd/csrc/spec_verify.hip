@@ -79,11 +79,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // LOW: key bits below the 16-bit bucket that no element of the format can vary
 template <int DT> struct Fmt;
 template <> struct Fmt<SV_BF16> {
-  static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8;
+  static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8, WAVES = 6;
   static constexpr uint32_t LOW = 0xffffu;   // low key bits of a bf16 value are all 0 or all 1
 };
 template <> struct Fmt<SV_F32> {
-  static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4;
+  static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4, WAVES = 7;
   static constexpr uint32_t LOW = 0u;
 };
 
@@ -100,20 +100,18 @@ static_assert(sizeof(TileRec) == 64, "tile record");
 
 // Published per group by its merging workgroup.
 struct GroupRec {
-  double s_t, s_d;         // row normalisers (relative to m_t, m_d)
-  float m_t, m_d;          // row maxima
+  float ot, od;            // sampling: offsets m * log2(e)/T + log2(s) of the target / draft row
   int32_t flags;           // SV_STATUS_* bits of this group's rows and token
+  int32_t argmax;          // greedy: top-1 index of the target row
   int32_t accept;          // 1 when the drafted token passed (pair groups)
-  int32_t argmax;          // top-1 index of the target row
-  int32_t pad;
+  int32_t ready;           // sampling: set to 1 once the fields above are visible
 };
+static_assert(sizeof(GroupRec) == 24, "group record");
 
-// Handed from the sequence assembly to the draw workgroups.
+// Written by the sequence assembly for the draw workgroups.
 struct SeqRec {
-  float ot, od;            // drawing row offsets m * log2(e)/T + log2(s) of its target / draft part
-  int32_t j;               // drawing position: residual for j < k, bonus for j == k
-  int32_t state;           // 0: not assembled yet; 1: a token to draw; 2: none (data error)
-  double u;                // the uniform of the draw
+  int32_t j;               // first rejection (k: none)
+  int32_t state;           // 0: not assembled yet; 1: assembled; 2: a data error, nothing to draw
 };
 constexpr int SREC_STRIDE = 256;       // bytes per sequence record: its pollers share no line
 
@@ -125,13 +123,14 @@ struct Params {
   int32_t *accepted_len, *out_tokens, *topk_idx, *status;
   float *topk_val, *lse_t, *lse_d, *p_tok, *q_tok;
   int32_t *fault;                      // bit 1: a wait gave up; bit 2: workspace not zero-filled
-  int32_t *garrive, *sarrive, *dpub, *ddone;    // counters, CTR int32 apart
+  int32_t *garrive, *sarrive, *ddone;          // counters, CTR int32 apart
   TileRec *recs;
   GroupRec *grec;
   SeqRec *srec;
   uint64_t *cand;                      // [group][tile][SLOTS] candidate keys, 0 = empty
   int32_t *ovf;                        // [group][tile] 1: more candidates than SLOTS
-  double *dtot;                        // [sequence][tile][2] drawing-row tile totals: residual, p
+  uint64_t *dtot;                      // [sequence][tile][2] drawing-row tile totals (residual, p) as
+                                       // tot_word: 0 until published
   int32_t B, k, V, nT;
   int32_t items;                       // streaming workgroups: B * (k + 1) * nT
   float T, sc;                         // sc = log2(e) / T
@@ -328,6 +327,14 @@ __device__ __forceinline__ int wait_at_least(const int32_t *p, int target, int32
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return v;
 }
+// A published fp64 value that is its own flag: the complement of its bits,
+// with -0 and NaN canonical, is never 0, the value of an empty slot.
+__device__ __forceinline__ uint64_t tot_word(double t) {
+  const double c = t == t ? t + 0.0 : __builtin_nan("");
+  return ~__builtin_bit_cast(uint64_t, c);
+}
+__device__ __forceinline__ double tot_value(uint64_t w) { return __builtin_bit_cast(double, ~w); }
+
 // Announce this workgroup's published data on a counter; returns the count
 // before it (the same value in every thread).
 __device__ __forceinline__ int arrive(int32_t *ctr, Smem &sm) {
@@ -390,9 +397,11 @@ template <int DT> __device__ __forceinline__ int dpos(int s, int w) {
   return ((int)threadIdx.x * NSEG + s) * Fmt<DT>::W + w;
 }
 
-// Stream one tile of a row into registers; entries past V read as -inf.
-// Vector s of a thread sits at tpos (vectors interleaved over the threads) or,
-// with TM, at dpos (each thread's vectors consecutive).
+// Load one tile of a row into registers; entries past V read as -inf.
+// Streaming (TM false): vector s of a thread sits at tpos (vectors interleaved
+// over the threads) and the loads are marked nontemporal, since each logit is
+// read once.  Draw (TM true): vector s sits at dpos (each thread's vectors
+// consecutive) with ordinary loads, which measured faster for this re-read.
 template <int DT, bool TM = false>
 __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool vec, u32x4 (&r)[NSEG]) {
   constexpr int E = Fmt<DT>::E, W = Fmt<DT>::W;
@@ -401,7 +410,8 @@ __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool ve
   for (int s = 0; s < NSEG; ++s) {
     const int64_t e0 = c0 + (TM ? dpos<DT>(s, 0) : tpos<DT>(s, 0));
     if (vec && e0 + W <= V) {
-      r[s] = __builtin_nontemporal_load((const u32x4 *)(row + e0 * E));
+      if (TM) r[s] = *(const u32x4 *)(row + e0 * E);
+      else r[s] = __builtin_nontemporal_load((const u32x4 *)(row + e0 * E));
     } else {
       u32x4 v;
 #pragma unroll
@@ -645,7 +655,6 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
   int st = 0, j = k;
   GroupRec mine = {};
   int32_t tok = 0;
-  float uu = 0.5f;
   for (int i0 = 0; i0 < k + 2; i0 += TPB) {
     const int i = i0 + tid;
     GroupRec r = {};
@@ -664,27 +673,17 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
       }
     }
     if (!(u >= 0.f && u < 1.f)) st |= SV_STATUS_BAD_UNIFORM;
-    if (i0 == 0) { mine = r; tok = x; uu = u; }
+    if (i0 == 0) { mine = r; tok = x; }
   }
   if (tid == 0 && ld_dev(P.fault)) st |= SV_STATUS_SYNC_TIMEOUT;
   block_or_min(st, j, sm);
-  // the drawing row's record and uniform reach every thread through LDS
-  const int ui = j < k ? k : k + 1;
-  if (small && tid == j) {
-    sm.dbc[4] = mine.s_t; sm.dbc[5] = mine.s_d;
-    sm.f[0][0] = mine.m_t; sm.f[0][1] = mine.m_d;
-    sm.bc[1] = mine.argmax;
+  // greedy: the argmax of row j reaches every thread through LDS
+  if (GREEDY) {
+    if (small && tid == j) sm.bc[1] = mine.argmax;
+    if (!small && tid == 0) sm.bc[1] = ld_rec(P.grec + (int64_t)b * K1 + j).argmax;
+    __syncthreads();
   }
-  if (small && tid == ui) sm.dbc[6] = (double)uu;
-  if (!small && tid == 0) {
-    const GroupRec rj = ld_rec(P.grec + (int64_t)b * K1 + j);
-    sm.dbc[4] = rj.s_t; sm.dbc[5] = rj.s_d; sm.f[0][0] = rj.m_t; sm.f[0][1] = rj.m_d; sm.bc[1] = rj.argmax;
-    sm.dbc[6] = GREEDY ? 0.0 : (double)P.uniforms[(int64_t)b * (k + 2) + ui];
-  }
-  __syncthreads();
-  const double s_t = sm.dbc[4], s_d = sm.dbc[5], u = sm.dbc[6];
-  const float m_t = sm.f[0][0], m_d = sm.f[0][1];
-  const int amax = sm.bc[1];
+  const int amax = GREEDY ? sm.bc[1] : -1;
   if (tid == 0) {
     if (P.status) P.status[b] = st;
     P.accepted_len[b] = st ? -1 : j;
@@ -695,18 +694,12 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
     if (!st && i == j && GREEDY) v = amax;
     if (st || i != j || GREEDY) P.out_tokens[(int64_t)b * K1 + i] = v;
   }
-  zero_recs(P.grec + (int64_t)b * K1, K1);
-  if (!GREEDY && tid == 0) {
-    // the draw workgroups wait for the state word: the record first, then it
-    SeqRec sr = {};
-    if (!st) {
-      sr.ot = (float)((double)m_t * P.scd + log2(s_t));
-      sr.od = j < k ? (float)((double)m_d * P.scd + log2(s_d)) : 0.f;
-      sr.j = j;
-      sr.u = u;
-    }
+  if (GREEDY) {
+    zero_recs(P.grec + (int64_t)b * K1, K1);
+  } else if (tid == 0) {
+    // the draw workgroups read the group records until they finish, and clear them
     SeqRec *rec = (SeqRec *)((char *)P.srec + (int64_t)b * SREC_STRIDE);
-    st_rec(rec, sr);
+    st_dev(&rec->j, j);
     stores_done();
     st_dev(&rec->state, st ? 2 : 1);
   }
@@ -720,13 +713,14 @@ __device__ __forceinline__ double exp2_split(double a) {
   return __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
 }
 
-// natural log of s > 0 to about 1e-7 absolute: exponent exactly, mantissa in
+// log2 of s > 0 to about 1e-7 absolute: exponent exactly, mantissa in
 // [1/2, 1) through the hardware fp32 log2
-__device__ __forceinline__ double log_split(double s) {
+__device__ __forceinline__ double log2_split(double s) {
   int e;
   const double m = __builtin_frexp(s, &e);
-  return ((double)e + (double)__builtin_amdgcn_logf((float)m)) * 0.6931471805599453;
+  return (double)e + (double)__builtin_amdgcn_logf((float)m);
 }
+__device__ __forceinline__ double log_split(double s) { return log2_split(s) * 0.6931471805599453; }
 
 // Row combine, acceptance decision and top-32 merge of group g (run by its last
 // tile once the others have published), then the sequence's arrival.
@@ -807,8 +801,9 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
       const double lg = log_split(lane == 0 ? S_t : S_d);
       if (lane == 0) {
         GroupRec gr;
-        gr.s_t = S_t; gr.s_d = S_d; gr.m_t = M_t; gr.m_d = M_d;
-        gr.flags = fl; gr.accept = acc; gr.argmax = -1; gr.pad = 0;
+        gr.ot = (float)((double)M_t * P.scd + log2_split(S_t));
+        gr.od = pair ? (float)((double)M_d * P.scd + log2_split(S_d)) : 0.f;
+        gr.flags = fl; gr.argmax = -1; gr.accept = acc; gr.ready = 0;
         st_rec(P.grec + g, gr);
         if (P.lse_t) P.lse_t[(int64_t)b * K1 + i] = (float)((double)M_t / (double)P.T + lg);
       }
@@ -817,10 +812,13 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         if (dst) dst[(int64_t)b * k + i] = (float)pv;
         if (lane == 1 && P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)M_d / (double)P.T + lg);
       }
-      // the group record is out: announce it to the sequence now (the top-32
-      // is not part of it)
+      // the group record is out: flag it for the draw and announce it to the
+      // sequence now (the top-32 is not part of it)
       stores_done();
-      if (lane == 0 && i != k) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
+      if (lane == 0) {
+        st_dev(&P.grec[g].ready, 1);
+        if (i != k) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
+      }
     }
 
     if (lane == 0) {
@@ -923,8 +921,8 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   }
   if (GREEDY && tid == 0) {
     GroupRec gr;
-    gr.s_t = 0.0; gr.s_d = 0.0; gr.m_t = M_t; gr.m_d = NEG_INF;
-    gr.flags = fl; gr.accept = 1; gr.argmax = sm.bc[6]; gr.pad = 0;
+    gr.ot = 0.f; gr.od = 0.f;
+    gr.flags = fl; gr.argmax = sm.bc[6]; gr.accept = 1; gr.ready = 0;
     st_rec(P.grec + g, gr);
   }
   // the group record is out: announce it, then clear the group's workspace
@@ -1009,18 +1007,21 @@ __device__ __forceinline__ float draw_mass(const u32x4 &vt, const u32x4 &vd, int
   return r > 0.f ? r : 0.f;
 }
 
-// Draw workgroup (b, c), dispatched after every streaming workgroup.  It waits
-// (bounded) for sequence b's assembly; if the sequence has a token to draw at
-// j, it publishes tile c's total mass of the drawing row (the residual
-// max(0, p_j - q_j) for j < k, p_k for j == k), waits for the row's other
-// tiles, finds the crossing tile of tau = u * R over the totals in tile order,
-// and if it holds that tile draws the first positive-mass element whose
-// cumulative mass exceeds tau (the tile's last positive-mass element should
-// rounding leave none).  A residual with no mass left (only through rounding)
-// is replaced by p_j in a second round.  Cumulative masses are the fixed-order
-// fp64 scan of fp32 per-vector sums, the same arithmetic for the totals and for
-// the draw.  A sequence's draw workgroups are consecutive, so each waits only
-// for workgroups dispatched with it or before it.  The last one to finish
+// Draw workgroup (b, c), dispatched after every streaming workgroup.  It
+// learns the drawing row j of sequence b from the group records as soon as it
+// is decided: the first rejected draft (all earlier ones accepted), or row k
+// once all k drafts are accepted; with more than 63 drafts it waits for the
+// sequence's assembly instead.  It publishes tile c's total mass of the drawing
+// row (the residual max(0, p_j - q_j) for j < k, p_k for j == k), waits for
+// the row's other tiles, finds the crossing tile of tau = u * R over the totals
+// in tile order, and if it holds that tile draws the first positive-mass
+// element whose cumulative mass exceeds tau (the tile's last positive-mass
+// element should rounding leave none), written once the assembly has found no
+// data error.  A residual with no mass left (only through rounding) is
+// replaced by p_j in a second round.  Cumulative masses are the fixed-order
+// fp64 scan of fp32 per-thread sums, the same arithmetic for the totals and
+// for the draw.  A sequence's draw workgroups are consecutive, so each waits
+// only for workgroups dispatched with it or before it.  The last one to finish
 // clears the sequence's state.
 template <int DT>
 __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &sm) {
@@ -1028,24 +1029,48 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int nT = P.nT, k = P.k, K1 = k + 1;
   SeqRec *rec = (SeqRec *)((char *)P.srec + (int64_t)b * SREC_STRIDE);
-  if (tid == 0) {
-    const int v = wait_at_least(&rec->state, 1, P.fault);
+  const GroupRec *grs = P.grec + (int64_t)b * K1;
+  if (wid == 0) {
     int j = -1;
-    if (v == 1) {
-      const SeqRec r = ld_rec(rec);
-      j = r.j;
-      if (j < 0 || j > k) { atomicOr(P.fault, 2); j = -1; }  // workspace not zero-filled
-      sm.f[2][0] = r.ot;
-      sm.f[2][1] = r.od;
-      sm.dbc[2] = r.u;
-    } else if (v > 2) {
-      atomicOr(P.fault, 2);
+    if (K1 <= 64) {
+      // lane i watches group i's (accept, ready) word
+      const uint64_t *word = (const uint64_t *)&grs[lane < K1 ? lane : 0].accept;
+      uint64_t w = lane < K1 ? ld_dev(word) : 0ull;
+      const uint64_t all = K1 == 64 ? ~0ull : (1ull << K1) - 1;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        const uint64_t rdy = __ballot(lane < K1 && (w >> 32) != 0) & all;
+        const uint64_t rej = __ballot(lane < k && (w >> 32) != 0 && (uint32_t)w == 0u);
+        const uint64_t nr = all & ~rdy;
+        const int fz = nr ? __builtin_ctzll(nr) : K1;              // first group not yet in
+        const uint64_t below = fz >= 64 ? ~0ull : (1ull << fz) - 1;
+        if (rej & below) { j = __builtin_ctzll(rej & below); break; }
+        if (fz == K1) { j = k; break; }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+          if (lane == 0) atomicOr(P.fault, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+        if (lane < K1 && (w >> 32) == 0) w = ld_dev(word);
+      }
+    } else if (lane == 0) {
+      const int v = wait_at_least(&rec->state, 1, P.fault);
+      if (v == 1 || v == 2) j = ld_dev(&rec->j);
+      if (j < 0 || j > k) { if (v > 0) atomicOr(P.fault, 2); j = -1; }
+      j = v == 1 ? j : -1;
     }
-    sm.bc[3] = j;
+    if (lane == 0) {
+      sm.bc[3] = j;
+      if (j >= 0) {
+        sm.f[2][0] = ld_dev(&grs[j].ot);
+        sm.f[2][1] = ld_dev(&grs[j].od);
+        sm.dbc[2] = (double)P.uniforms[(int64_t)b * (k + 2) + (j < k ? k : k + 1)];
+      }
+    }
   }
   __syncthreads();
   const int j = sm.bc[3];
-  double *tot = P.dtot + (int64_t)b * nT * 2;
+  uint64_t *tot = P.dtot + (int64_t)b * nT * 2;
   if (j >= 0) {
     const bool resid = j < k;
     const float ot = sm.f[2][0], od = sm.f[2][1];
@@ -1078,17 +1103,21 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
         for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rd[s], w, rmode, o1, o2, P.sc);
       mine = a;
       const double t = block_scan_d((double)a, base, sm);
-      if (tid == 0) st_dev(tot + 2 * c + round, t);
-      block_stores_done();
-      if (tid == 0) {
-        add_dev_noret(P.dpub + (int64_t)b * CTR, 1);
-        const int v = wait_at_least(P.dpub + (int64_t)b * CTR, (round + 1) * nT, P.fault);
-        if (v > (round + 1) * nT) atomicOr(P.fault, 2);
-      }
-      __syncthreads();
-      // the crossing tile, from the totals in tile order (wave 0)
+      if (tid == 0) st_dev(tot + 2 * c + round, tot_word(t));
+      // the crossing tile, from the totals in tile order (wave 0, lane l
+      // polling tile l's slot until every tile has published)
       if (wid == 0) {
-        const double cum = wave_scan_d(lane < nT ? ld_dev(tot + 2 * lane + round) : 0.0);
+        uint64_t tw = lane < nT ? ld_dev(tot + 2 * lane + round) : ~0ull;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__ballot(tw == 0)) {
+          if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+            if (lane == 0) atomicOr(P.fault, 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+          if (tw == 0) tw = ld_dev(tot + 2 * lane + round);
+        }
+        const double cum = wave_scan_d(lane < nT ? tot_value(tw) : 0.0);
         const double R = readlane_d(cum, 63);
         const double tau = u * R;
         const uint64_t h = __ballot(lane < nT && cum > tau);
@@ -1135,7 +1164,9 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
           l = sm.i[3][w] > l ? sm.i[3][w] : l;
         }
         const int pos = f != 0x7fffffff ? f : l;
-        P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+        // the token stands unless the assembly found a data error
+        if (wait_at_least(&rec->state, 1, P.fault) == 1)
+          P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
       }
     }
   }
@@ -1145,16 +1176,17 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
     if ((old < 0 || old >= nT) && tid == 0) atomicOr(P.fault, 2);
     return;
   }
-  for (int q = tid; q < 2 * nT; q += TPB) st_dev(tot + q, 0.0);
+  // (the assembly has read the group records once it has set its state)
+  if (tid == 0) wait_at_least(&rec->state, 1, P.fault);
+  __syncthreads();
+  for (int q = tid; q < 2 * nT; q += TPB) st_dev(tot + q, (uint64_t)0);
   zero_recs(rec, 1);
-  if (tid == 0) {
-    st_dev(P.dpub + (int64_t)b * CTR, 0);
-    st_dev(P.ddone + (int64_t)b * CTR, 0);
-  }
+  zero_recs(P.grec + (int64_t)b * K1, K1);
+  if (tid == 0) st_dev(P.ddone + (int64_t)b * CTR, 0);
 }
 
 template <int DT, bool GREEDY>
-__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) void sv_verify(Params P) {
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(Fmt<DT>::WAVES, 8))) void sv_verify(Params P) {
   __shared__ Smem sm;
   constexpr int W = Fmt<DT>::W, TILE = Fmt<DT>::TILE;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1299,7 +1331,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
 
 // ---------------------------------------------------------------- host side
 struct Layout {
-  size_t fault, garrive, sarrive, dpub, ddone, recs, grec, srec, cand, ovf, dtot, total;
+  size_t fault, garrive, sarrive, ddone, recs, grec, srec, cand, ovf, dtot, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1314,7 +1346,6 @@ Layout layout_for(int B, int k, int V, int dtype) {
   L.fault = o;   o = align256(o + sizeof(int32_t));     // fixed header, same offset for every shape
   L.garrive = o; o = align256(o + groups * CTR * sizeof(int32_t));
   L.sarrive = o; o = align256(o + (size_t)B * CTR * sizeof(int32_t));
-  L.dpub = o;    o = align256(o + (size_t)B * CTR * sizeof(int32_t));
   L.ddone = o;   o = align256(o + (size_t)B * CTR * sizeof(int32_t));
   L.recs = o;    o = align256(o + groups * nT * sizeof(TileRec));
   L.grec = o;    o = align256(o + groups * sizeof(GroupRec));
@@ -1412,14 +1443,13 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   P.fault = (int32_t *)(ws + L.fault);
   P.garrive = (int32_t *)(ws + L.garrive);
   P.sarrive = (int32_t *)(ws + L.sarrive);
-  P.dpub = (int32_t *)(ws + L.dpub);
   P.ddone = (int32_t *)(ws + L.ddone);
   P.recs = (TileRec *)(ws + L.recs);
   P.grec = (GroupRec *)(ws + L.grec);
   P.srec = (SeqRec *)(ws + L.srec);
   P.cand = (uint64_t *)(ws + L.cand);
   P.ovf = (int32_t *)(ws + L.ovf);
-  P.dtot = (double *)(ws + L.dtot);
+  P.dtot = (uint64_t *)(ws + L.dtot);
   P.B = s.B;
   P.k = s.k;
   P.V = s.V;
