@@ -8,11 +8,10 @@ Cache) rotate so every step reads its logits from HBM.
 
 Prints one JSON line.  value = algorithmic logit bytes (each logit read once,
 B(2k+1)V * 2 bytes) / wall time per step, inputs resident in HBM.  roofline =
-the same bytes / the duration of the streaming kernel sv_verify, the one that
-reads every logit (HIP events the library records right before and after it
-on the launch stream), against the 8 TB/s HBM peak.  The step also runs the
-small draw kernel.  cpu_baseline = the plain C oracle on the host over a
-bounded number of whole batches.
+the same bytes / the duration of the one kernel launch sv_verify (streaming,
+merges, assembly and draw; HIP events the library records right before and
+after it on the launch stream), against the 8 TB/s HBM peak.  cpu_baseline =
+the plain C oracle on the host over a bounded number of whole batches.
 
   python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|tiny]
   python bench.py --copy-calib    # a plain 1 GiB device copy, for HBM counter calibration
@@ -145,7 +144,7 @@ def main():
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps over {copies} input copies",
           file=sys.stderr, flush=True)
 
-    # streaming-kernel duration: the library records an event pair around it on the launch stream
+    # kernel duration: the library records an event pair around its launch on the launch stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in ev:                      # torch creates the underlying events on first record
         a.record(stream)

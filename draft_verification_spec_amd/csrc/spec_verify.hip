@@ -1,10 +1,10 @@
 // spec_verify.hip -- speculative-sampling verification for gfx950 (MI355X).
 //
-// Two launches: sv_verify, one workgroup per (group, tile), streams the logits
-// and assembles every sequence; in sampling mode sv_draw, one workgroup per
-// (sequence, tile), then draws the residual or bonus token.
+// One launch of sv_verify.  Its first workgroups, one per (group, tile), stream
+// the logits and assemble every sequence; in sampling mode one workgroup per
+// (sequence, tile) follows and draws the residual or bonus token.
 //
-//  sv_verify  A group is, for i < k, the pair (target row i, draft row i) of a
+//  streaming  A group is, for i < k, the pair (target row i, draft row i) of a
 //             sequence and, for i == k, target row k alone; in greedy mode every
 //             group is one target row.  Tiles are fixed 16 KB slices of a row
 //             (8192 bf16 or 4096 fp32 entries).  Each workgroup streams its
@@ -22,27 +22,31 @@
 //             element from below; candidates at or above it are ranked, and a
 //             tile whose candidate threshold lies above the bound (it may hold
 //             further elements above it) is rescanned, as is a tile whose
-//             candidates overflowed their slots.
+//             candidates overflowed their slots.  The group record (offsets of
+//             the row's log-normaliser, flags, decision) is flagged ready as
+//             soon as the decision is made.
 //             The merge of row k (dispatched after rows 0..k-1) waits for the
 //             sequence's other groups and assembles it: the first rejection j
 //             (greedy: the first draft that differs from the argmax), the
-//             tokens, and the position and normalisers of the token to draw.
-//  sv_draw    Each workgroup of a sequence publishes one tile's total mass of
-//             the drawing row: the residual max(0, p - q) of pair row j after a
-//             rejection, p of row k after k acceptances.  Once all tiles of the
-//             row are in, every workgroup finds the crossing tile of u * R over
+//             tokens, and whether the sequence has a data error.
+//  draw       The draw workgroups of a sequence learn the drawing row from the
+//             group records as soon as it is decided: pair row j after a
+//             rejection (residual max(0, p - q)), row k after k acceptances
+//             (p).  Each publishes one tile's total mass; once all tiles of
+//             the row are in, every one finds the crossing tile of u * R over
 //             the totals in tile order, and the one that holds it draws the
 //             token from its registers.
 //
-// In sv_verify a workgroup only ever waits for workgroups of a lower index,
-// which the hardware dispatches first; in sv_draw for the other workgroups of
-// its sequence, dispatched with it.  Every wait is bounded in time: a wait that
-// gives up sets the fault word (reported as SV_STATUS_SYNC_TIMEOUT) and the
-// kernel still finishes.  Data moves between workgroups through the workspace
-// with device-scope write-through stores and device-scope loads, ordered by
-// waiting for the stores to complete before the counter or flag that announces
-// them is written.  Wave-level reductions and scans run on DPP row shifts and
-// broadcasts in a fixed order, so every reduction is deterministic.
+// A streaming workgroup only ever waits for workgroups of a lower index, which
+// the hardware dispatches first; a draw workgroup for streaming workgroups and
+// for the other draw workgroups of its sequence, dispatched with it.  Every
+// wait is bounded in time: a wait that gives up sets the fault word (reported
+// as SV_STATUS_SYNC_TIMEOUT) and the kernel still finishes.  Data moves
+// between workgroups through the workspace with device-scope write-through
+// stores and device-scope loads, ordered by waiting for the stores to complete
+// before the counter or flag that announces them is written.  Wave-level
+// reductions and scans run on DPP row shifts and broadcasts in a fixed order,
+// so every reduction is deterministic.
 //
 // Acceptance test, residual and bonus draw follow the ReSpec notes ("2 .
 // background": one-shot acceptance test Eq.1, residual max(0,p-q)/sum); the
@@ -645,7 +649,7 @@ template <int DT, bool GREEDY> __device__ __forceinline__ Geo geo(const Params &
 
 // Sequence assembly (run by the merge of row k once the sequence's other
 // groups have published): status, first rejection j, and the tokens; greedy
-// emits everything, sampling hands the drawing row to sv_draw.
+// emits everything, sampling leaves the drawn token to the draw workgroups.
 template <int DT, bool GREEDY>
 __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
   const int tid = threadIdx.x;

@@ -86,9 +86,9 @@ typedef struct {
     float *lse_draft;    /* [B,k]   ln sum_x exp(d_x / T)   (sampling only) */
     float *p_tok;        /* [B,k]   p_i(x_i)                (sampling only) */
     float *q_tok;        /* [B,k]   q_i(x_i)                (sampling only) */
-    void *event_begin;   /* hipEvent_t recorded on the stream right before the streaming
-                            kernel (the one that reads every logit), or NULL */
-    void *event_end;     /* hipEvent_t recorded right after it (before the draw kernel), or NULL */
+    void *event_begin;   /* hipEvent_t recorded on the stream right before the kernel
+                            launch, or NULL */
+    void *event_end;     /* hipEvent_t recorded right after it, or NULL */
 } sv_aux_t;
 
 /* Bytes of device workspace one call with this shape needs. */
@@ -123,10 +123,11 @@ size_t spec_verify_workspace_bytes(const sv_shape_t *shape);
  *   row, bad uniform) cannot be seen without a device sync; they set the
  *   SV_STATUS_* bits of that sequence and make its accepted_len and
  *   out_tokens -1.
- * Execution: one streaming kernel (every logit read once; per-tile statistics
- *   and candidates, per-group merges, per-sequence assembly), then in sampling
- *   mode a draw kernel (residual or bonus draw).  Inside the streaming kernel a
- *   workgroup only ever waits for workgroups of lower index, with a time bound.
+ * Execution: one kernel launch.  Its streaming workgroups read every logit
+ *   once (per-tile statistics and candidates, per-group merges, per-sequence
+ *   assembly); in sampling mode draw workgroups follow (residual or bonus
+ *   draw).  A workgroup waits only for workgroups of lower index or for the
+ *   other draw workgroups of its sequence, always with a time bound.
  * The library allocates no memory and keeps no per-call state; it is safe to
  * call from several host threads with separate workspaces.
  */
