@@ -14,6 +14,7 @@ after it on the launch stream), against the 8 TB/s HBM peak.  cpu_baseline =
 the plain C oracle on the host over a bounded number of whole batches.
 
   python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|tiny]
+  python bench.py --workload kd   # the drafter distillation step over the stored top-32 (its own metric)
   python bench.py --copy-calib    # a plain 1 GiB device copy, for HBM counter calibration
 """
 import argparse
@@ -102,6 +103,95 @@ def copy_calib():
     print(json.dumps({"copy_calib_bytes_per_launch_read": n, "write": n, "launches": 3}))
 
 
+KD_METRIC = "kd drafter-logit read + gradient write GB/s (% HBM peak) at N=4096 V=151936 bf16"
+
+
+def bench_kd(args):
+    """The reward-weighted distillation step: one sv_kd launch over the rollout
+    batch's stored positions (N=4096 rows of V=151936 bf16 drafter logits),
+    loss and bf16 gradient.  value = (logits read once + gradient written once)
+    / wall time per step."""
+    import torch
+    import draft_verification_spec_amd as sv
+    import sv_inputs
+
+    w = sv_inputs.kd_rollout() if args.workload == "kd" else sv_inputs.kd_small()
+    print(f"[bench] workload {w.name} N={w.N} V={w.V} bf16, grad bf16", file=sys.stderr, flush=True)
+    z, tv, ti, rs, rw = sv.kd_to_device(w)
+    alg = w.alg_bytes(grad_bytes=2)
+    copies = args.copies or max(1, -(-4 * MALL_BYTES // (w.N * w.V * w.elem_bytes)))
+    zs = [z] + [z.clone() for _ in range(copies - 1)]
+    shape = sv.make_kd_shape(w.N, w.V, sv.SV_BF16, sv.SV_BF16, w.S, w.group, w.w_max)
+    ws = sv.workspace_for(z.device, sv.sv_kd_workspace_bytes(shape))
+    dev = z.device
+    kl = torch.empty(w.N, dtype=torch.float32, device=dev)
+    wt = torch.empty_like(kl)
+    st = torch.empty(w.N, dtype=torch.int32, device=dev)
+    loss = torch.zeros(1, dtype=torch.float64, device=dev)
+    grad = torch.empty(w.N, w.V, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        rc = sv.sv_kd(shape, zs[i % copies].data_ptr(), tv.data_ptr(), ti.data_ptr(), rs.data_ptr(), rw.data_ptr(),
+                      kl.data_ptr(), wt.data_ptr(), st.data_ptr(), loss.data_ptr(), grad.data_ptr(), ws.data_ptr(),
+                      ws.numel(), stream.cuda_stream)
+        if rc != sv.SV_OK:
+            raise sv.SpecVerifyError(rc)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps over {copies} input copies",
+          file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    kern_avg = float(kern_ms.mean())
+    achieved = alg / (kern_avg * 1e-3) / 1e9
+    line = {
+        "metric": KD_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Philox drafter logits and stored top-32 entries of the workload's shape)",
+        "config": {"workload": f"{w.name} N={w.N} V={w.V} bf16 grad bf16", "N": w.N, "V": w.V, "S": w.S,
+                   "group": w.group, "alg_bytes_per_step": alg, "input_copies_rotated": copies},
+        "rows_per_s": round(w.N / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "sv_kd_kernel",
+                     "kernel_us_mean": round(kern_avg * 1e3, 3),
+                     "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, q)) * 1e3, 3) for q in (10, 50, 90)]},
+        "loss": float(loss.cpu()[0]),
+    }
+    if not args.no_cpu:
+        import oracle
+        oracle.build()
+        rows = np.arange(w.N)                   # the whole batch: a few seconds of oracle work
+        t1 = time.perf_counter()
+        o = oracle.kd_workload(w, grad=True, rows=rows)
+        dt = time.perf_counter() - t1
+        sample_bytes = len(rows) * w.V * (w.elem_bytes + 2)
+        g_kl = kl.cpu().numpy()[rows]
+        ok = o.status == 0
+        line["cpu_baseline"] = {
+            "value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {len(rows)} rows of the batch (loss and fp64 gradient), {dt:.2f} s, single thread of "
+                      f"{os.cpu_count()} host threads", "rows_per_s": round(len(rows) / dt, 2)}
+        line["parity_vs_oracle"] = {"rows": int(len(rows)), "max_abs_kl_err": float(np.max(np.abs(g_kl[ok] - o.kl[ok]))),
+                                    "status_equal": bool(np.array_equal(st.cpu().numpy()[rows], o.status))}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +208,8 @@ def main():
         sys.exit(2)
     if args.copy_calib:
         return copy_calib()
+    if args.workload in ("kd", "kd_small"):
+        return bench_kd(args)
 
     import torch
     import draft_verification_spec_amd as sv

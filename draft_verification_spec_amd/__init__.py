@@ -1,4 +1,5 @@
-"""Python binding of the spec_verify C ABI (include/spec_verify.h).
+"""Python binding of the library's C ABI: spec_verify (include/spec_verify.h)
+and sv_kd (include/sv_kd.h).
 
 Argument marshalling only: every step of the verification runs in the HIP
 library libspec_verify.so built next to this file.  PyTorch supplies device
@@ -16,6 +17,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspec_verify.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "spec_verify.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_HERE), "include", "sv_kd.h")]
 
 SV_F32, SV_BF16 = 0, 1
 TOPK = 32
@@ -36,6 +38,15 @@ class sv_aux_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_void_p), ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p),
                 ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p),
                 ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p)]
+
+
+class sv_kd_shape_t(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("row_stride", ctypes.c_int64), ("S", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("w_max", ctypes.c_float)]
+
+
+KD_BAD_INDEX, KD_NAN, KD_POSINF, KD_EMPTY, KD_SYNC_TIMEOUT = 1, 2, 4, 8, 32
 
 
 class SpecVerifyError(RuntimeError):
@@ -62,14 +73,21 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify.argtypes = [ctypes.POINTER(sv_shape_t), P, P, P, P, P, P, P, P,
                                     ctypes.POINTER(sv_aux_t), P, ctypes.c_size_t, P]
         lib.spec_verify.restype = ctypes.c_int
+        lib.sv_kd_workspace_bytes.argtypes = [ctypes.POINTER(sv_kd_shape_t)]
+        lib.sv_kd_workspace_bytes.restype = ctypes.c_size_t
+        lib.sv_kd.argtypes = [ctypes.POINTER(sv_kd_shape_t), P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.sv_kd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
 def declared_functions() -> list:
-    """Names of the functions include/spec_verify.h declares."""
-    text = open(HEADER_PATH).read()
-    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(spec_verify\w*)\s*\(", text, flags=re.M)
+    """Names of the functions include/spec_verify.h and include/sv_kd.h declare."""
+    names = []
+    for path in HEADER_PATHS:
+        text = open(path).read()
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*((?:spec_verify|sv_kd)\w*)\s*\(", text, flags=re.M)
+    return names
 
 
 def make_shape(B, k, V, dtype, temperature, target_row_stride=0, draft_row_stride=0) -> sv_shape_t:
@@ -214,3 +232,86 @@ def to_device(w, device="cuda"):
         d = torch.from_numpy(w.draft)
     return (t.to(device), d.to(device), torch.from_numpy(w.draft_tokens).to(device),
             torch.from_numpy(w.uniforms).to(device))
+
+
+# ---------------------------------------------------------------- distillation
+KDResult = namedtuple("KDResult", "kl weight status loss grad")
+
+
+def make_kd_shape(N, V, dtype, grad_dtype, S, group, w_max=float("inf"), row_stride=0) -> sv_kd_shape_t:
+    return sv_kd_shape_t(int(N), int(V), int(dtype), int(grad_dtype), int(row_stride), int(S), int(group),
+                         float(w_max))
+
+
+def sv_kd_workspace_bytes(shape: sv_kd_shape_t) -> int:
+    return int(load_library().sv_kd_workspace_bytes(ctypes.byref(shape)))
+
+
+def sv_kd(shape: Optional[sv_kd_shape_t], draft_logits, topk_val, topk_idx, row_sample, rewards, kl, weight, status,
+          loss, grad, workspace, workspace_bytes, stream) -> int:
+    """Direct call of the C entry point with raw device addresses (ints or None)."""
+    return int(load_library().sv_kd(None if shape is None else ctypes.byref(shape), draft_logits, topk_val, topk_idx,
+                                    row_sample, rewards, kl, weight, status, loss, grad, workspace,
+                                    int(workspace_bytes), stream))
+
+
+def kd(draft_logits, topk_val, topk_idx, row_sample, rewards, group: int, *, w_max: float = float("inf"),
+       grad: bool = True, grad_dtype=None, workspace=None, stream=None, events=None) -> KDResult:
+    """Reward-weighted distillation loss (and gradient) on torch tensors of one
+    device.  draft_logits [N,V] float32 or bfloat16 (unit element stride);
+    topk_val [N,32] float32; topk_idx [N,32] int32; row_sample [N] int32;
+    rewards [S] float32.  grad_dtype defaults to the logits' dtype.  events:
+    optional pair of torch.cuda.Event recorded around the kernel."""
+    import torch
+    if draft_logits.dim() != 2 or draft_logits.stride(1) != 1:
+        raise ValueError("draft_logits must be [N, V] with unit element stride")
+    N, V = draft_logits.shape
+    dev = draft_logits.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    dts = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
+    if draft_logits.dtype not in dts:
+        raise TypeError("draft logits must be float32 or bfloat16")
+    dt = dts[draft_logits.dtype]
+    gtorch = grad_dtype if grad_dtype is not None else draft_logits.dtype
+    gdt = dts[gtorch]
+    tv = topk_val.to(device=dev, dtype=torch.float32).contiguous()
+    ti = topk_idx.to(device=dev, dtype=torch.int32).contiguous()
+    rs = row_sample.to(device=dev, dtype=torch.int32).contiguous()
+    rw = rewards.to(device=dev, dtype=torch.float32).contiguous()
+    if tuple(tv.shape) != (N, TOPK) or tuple(ti.shape) != (N, TOPK) or tuple(rs.shape) != (N,):
+        raise ValueError("topk_val/topk_idx must be [N, 32] and row_sample [N]")
+    shape = make_kd_shape(N, V, dt, gdt, rw.numel(), group, w_max, draft_logits.stride(0) if N > 1 else V)
+    f32 = dict(dtype=torch.float32, device=dev)
+    kl = torch.empty(N, **f32)
+    wt = torch.empty(N, **f32)
+    st = torch.empty(N, dtype=torch.int32, device=dev)
+    loss = torch.zeros(1, dtype=torch.float64, device=dev)
+    g = torch.empty(N, V, dtype=gtorch, device=dev) if grad else None
+    nbytes = sv_kd_workspace_bytes(shape)
+    ws = workspace if workspace is not None else workspace_for(dev, nbytes)
+    cur = torch.cuda.current_stream(dev)
+    if stream is None:
+        stream = cur.cuda_stream
+    if events is not None:
+        if stream != cur.cuda_stream:
+            raise ValueError("events are recorded on the current stream: launch there")
+        events[0].record(cur)
+    rc = sv_kd(shape, draft_logits.data_ptr(), tv.data_ptr(), ti.data_ptr(), rs.data_ptr(), rw.data_ptr(),
+               kl.data_ptr(), wt.data_ptr(), st.data_ptr(), loss.data_ptr(), None if g is None else g.data_ptr(),
+               ws.data_ptr(), ws.numel(), stream)
+    if events is not None:
+        events[1].record(cur)
+    if rc != SV_OK:
+        raise SpecVerifyError(rc)
+    return KDResult(kl, wt, st, loss, g)
+
+
+def kd_to_device(w, device="cuda"):
+    """Upload an sv_inputs.KDWorkload: (logits, topk_val, topk_idx, row_sample, rewards) tensors."""
+    import numpy as np
+    import torch
+    z = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16) if w.dtype == SV_BF16 \
+        else torch.from_numpy(w.logits)
+    return (z.to(device), torch.from_numpy(w.topk_val).to(device), torch.from_numpy(w.topk_idx).to(device),
+            torch.from_numpy(w.row_sample).to(device), torch.from_numpy(w.rewards).to(device))

@@ -1,10 +1,12 @@
-"""Compile the HIP library for gfx950 in-tree (libspec_verify.so next to this file)."""
+"""Compile the HIP library for gfx950 in-tree (libspec_verify.so next to this file):
+the verification kernel and the distillation kernel."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "spec_verify.hip")
+SRCS = [SRC, os.path.join(HERE, "csrc", "sv_kd.hip")]
 LIB = os.path.join(HERE, "libspec_verify.so")
 HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 
@@ -19,7 +21,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False, extra=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

@@ -60,37 +60,18 @@
 #include <string.h>
 
 #include "spec_verify.h"
+#include "sv_device.h"
 
 namespace {
 
-constexpr int TPB = 256;               // threads per workgroup (4 waves of 64)
-constexpr int NWAVE = TPB / 64;
-constexpr int NSEG = 4;                // 16-byte vectors per thread per row
+using namespace sv_dev;
+
 constexpr int LIST = 8;                // lane maxima a tile record keeps
 constexpr int SLOTS = 32;              // candidate slots per tile
 constexpr int MERGE_CAP = 512;         // candidates a row merge ranks in LDS
 constexpr int TOPK = SV_TOPK;
 constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
-constexpr float NEG_INF = -__builtin_inff();
-constexpr uint64_t SPIN_TICKS = 20000000;          // bounded waits give up after 0.2 s (100 MHz clock)
-constexpr int CTR = 64;                            // int32 per counter: each on its own 256 bytes, so
-                                                   // polling one never contends with another
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// E: bytes per element; W: elements per 16-byte vector; TILE: elements per tile;
-// LOW: key bits below the 16-bit bucket that no element of the format can vary
-template <int DT> struct Fmt;
-template <> struct Fmt<SV_BF16> {
-  static constexpr int E = 2, W = 8, TILE = TPB * NSEG * 8, WAVES = 6;
-  static constexpr uint32_t LOW = 0xffffu;   // low key bits of a bf16 value are all 0 or all 1
-};
-template <> struct Fmt<SV_F32> {
-  static constexpr int E = 4, W = 4, TILE = TPB * NSEG * 4, WAVES = 7;
-  static constexpr uint32_t LOW = 0u;
-};
-
 // Published per (group, tile) by the stream workgroups; 8 words.
 struct TileRec {
   float m_t, m_d;          // tile max of the target / draft row part
@@ -181,73 +162,6 @@ __device__ __forceinline__ float cand_value(uint64_t k) {
   return (k & 1u) ? -0.0f : key_value((uint32_t)(k >> 32));
 }
 
-// ---- wave primitives on DPP.  A lane whose DPP source is outside its row, or
-// that the row / bank mask leaves out, receives the identity `old`.
-template <int CTRL, int RM, int BM> __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, RM, BM, false);
-}
-template <int CTRL, int RM, int BM> __device__ __forceinline__ double dpp_d(double v) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = dpp<CTRL, RM, BM>(0u, (uint32_t)u);
-  const uint32_t hi = dpp<CTRL, RM, BM>(0u, (uint32_t)(u >> 32));
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
-}
-__device__ __forceinline__ double readlane_d(double v, int l) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  return __builtin_bit_cast(double, ((uint64_t)readlane((uint32_t)(u >> 32), l) << 32) | readlane((uint32_t)u, l));
-}
-// Reduction over the wave, returned to every lane: neighbours, then groups of
-// 4 and 8 and whole rows of 16, then the four rows (lane 63 ends with all).
-template <class Op> __device__ __forceinline__ uint32_t wave_red(uint32_t v, uint32_t id, Op op) {
-  v = op(v, dpp<0x111, 0xf, 0xf>(id, v));   // row_shr:1
-  v = op(v, dpp<0x112, 0xf, 0xf>(id, v));   // row_shr:2
-  v = op(v, dpp<0x114, 0xf, 0xe>(id, v));   // row_shr:4, banks 1-3
-  v = op(v, dpp<0x118, 0xf, 0xc>(id, v));   // row_shr:8, banks 2-3
-  v = op(v, dpp<0x142, 0xa, 0xf>(id, v));   // row_bcast:15 into rows 1, 3
-  v = op(v, dpp<0x143, 0xc, 0xf>(id, v));   // row_bcast:31 into rows 2, 3
-  return readlane(v, 63);
-}
-struct OpMaxI { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return (int)a > (int)b ? a : b; } };
-struct OpMinI { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return (int)a < (int)b ? a : b; } };
-struct OpOr { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
-struct OpMaxF {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
-    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
-  }
-};
-__device__ __forceinline__ int wave_max_i(int v) { return (int)wave_red((uint32_t)v, 0x80000000u, OpMaxI()); }
-__device__ __forceinline__ int wave_min_i(int v) { return (int)wave_red((uint32_t)v, 0x7fffffffu, OpMinI()); }
-__device__ __forceinline__ int wave_or(int v) { return (int)wave_red((uint32_t)v, 0u, OpOr()); }
-__device__ __forceinline__ float wave_max_f(float v) {
-  return __uint_as_float(wave_red(__float_as_uint(v), 0xff800000u, OpMaxF()));
-}
-__device__ __forceinline__ double wave_sum_d(double v) {
-  v += dpp_d<0x111, 0xf, 0xf>(v);
-  v += dpp_d<0x112, 0xf, 0xf>(v);
-  v += dpp_d<0x114, 0xf, 0xe>(v);
-  v += dpp_d<0x118, 0xf, 0xc>(v);
-  v += dpp_d<0x142, 0xa, 0xf>(v);
-  v += dpp_d<0x143, 0xc, 0xf>(v);
-  return readlane_d(v, 63);
-}
-// Inclusive prefix sum over the wave's lanes: windows of 4 within a row, then
-// 8 and 16, then earlier rows.
-__device__ __forceinline__ double wave_scan_d(double x) {
-  double v = x + dpp_d<0x111, 0xf, 0xf>(x);
-  v += dpp_d<0x112, 0xf, 0xf>(x);
-  v += dpp_d<0x113, 0xf, 0xf>(x);
-  v += dpp_d<0x114, 0xf, 0xe>(v);
-  v += dpp_d<0x118, 0xf, 0xc>(v);
-  v += dpp_d<0x142, 0xa, 0xf>(v);
-  v += dpp_d<0x143, 0xc, 0xf>(v);
-  return v;
-}
-// value of the previous lane of the wave (0 in lane 0)
-__device__ __forceinline__ double wave_prev_d(double v) { return dpp_d<0x138, 0xf, 0xf>(v); }
-
 // The two largest keys of the wave's lanes (equal keys of different lanes
 // count twice; 0 where fewer lanes hold a nonzero key), in every lane.
 __device__ __forceinline__ void wave_top2(uint32_t key, uint32_t &k1, uint32_t &k2) {
@@ -270,262 +184,6 @@ __device__ __forceinline__ void wave_top2(uint32_t key, uint32_t &k1, uint32_t &
   k1 = readlane(a, 63);
   k2 = readlane(c, 63);
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-  v += (int)dpp<0x111, 0xf, 0xf>(0u, (uint32_t)v);
-  v += (int)dpp<0x112, 0xf, 0xf>(0u, (uint32_t)v);
-  v += (int)dpp<0x114, 0xf, 0xe>(0u, (uint32_t)v);
-  v += (int)dpp<0x118, 0xf, 0xc>(0u, (uint32_t)v);
-  v += (int)dpp<0x142, 0xa, 0xf>(0u, (uint32_t)v);
-  v += (int)dpp<0x143, 0xc, 0xf>(0u, (uint32_t)v);
-  return (int)readlane((uint32_t)v, 63);
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-  v += __uint_as_float(dpp<0x111, 0xf, 0xf>(0u, __float_as_uint(v)));
-  v += __uint_as_float(dpp<0x112, 0xf, 0xf>(0u, __float_as_uint(v)));
-  v += __uint_as_float(dpp<0x114, 0xf, 0xe>(0u, __float_as_uint(v)));
-  v += __uint_as_float(dpp<0x118, 0xf, 0xc>(0u, __float_as_uint(v)));
-  v += __uint_as_float(dpp<0x142, 0xa, 0xf>(0u, __float_as_uint(v)));
-  v += __uint_as_float(dpp<0x143, 0xc, 0xf>(0u, __float_as_uint(v)));
-  return __uint_as_float(readlane(__float_as_uint(v), 63));
-}
-
-// Device-scope accesses: loads see the latest device-visible value; stores are
-// written through to the device coherence point.  No cache maintenance.
-template <class T> __device__ __forceinline__ T ld_dev(const T *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <class T> __device__ __forceinline__ void st_dev(T *p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int add_dev(int32_t *p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void add_dev_noret(int32_t *p, int v) {
-  (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until this wave's earlier memory accesses have completed (and keep the
-// compiler from moving memory accesses across the wait).
-__device__ __forceinline__ void stores_done() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-// All of the workgroup's stores have completed (every wave waited for its own).
-__device__ __forceinline__ void block_stores_done() {
-  stores_done();
-  __syncthreads();
-}
-// Bounded wait of one thread until *p >= target.  Returns the value seen;
-// on timeout sets fault bit 1 and returns what it last saw.
-__device__ __forceinline__ int wait_at_least(const int32_t *p, int target, int32_t *fault) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  int v = ld_dev(p);
-  while (v < target) {
-    if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
-      atomicOr(fault, 1);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(8);
-    v = ld_dev(p);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  return v;
-}
-// A published fp64 value that is its own flag: the complement of its bits,
-// with -0 and NaN canonical, is never 0, the value of an empty slot.
-__device__ __forceinline__ uint64_t tot_word(double t) {
-  const double c = t == t ? t + 0.0 : __builtin_nan("");
-  return ~__builtin_bit_cast(uint64_t, c);
-}
-__device__ __forceinline__ double tot_value(uint64_t w) { return __builtin_bit_cast(double, ~w); }
-
-// Announce this workgroup's published data on a counter; returns the count
-// before it (the same value in every thread).
-__device__ __forceinline__ int arrive(int32_t *ctr, Smem &sm) {
-  block_stores_done();
-  if (threadIdx.x == 0) sm.bc[7] = add_dev(ctr, 1);
-  __syncthreads();
-  const int old = sm.bc[7];
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  return old;
-}
-// Records move as 64-bit words.
-template <class T> __device__ __forceinline__ void st_rec(T *dst, const T &v) {
-  static_assert(sizeof(T) % 8 == 0, "record size");
-  const uint64_t *s = (const uint64_t *)&v;
-  uint64_t *d = (uint64_t *)dst;
-#pragma unroll
-  for (int w = 0; w < (int)(sizeof(T) / 8); ++w) st_dev(d + w, s[w]);
-}
-template <class T> __device__ __forceinline__ T ld_rec(const T *src) {
-  static_assert(sizeof(T) % 8 == 0, "record size");
-  T v;
-  uint64_t *d = (uint64_t *)&v;
-  const uint64_t *s = (const uint64_t *)src;
-#pragma unroll
-  for (int w = 0; w < (int)(sizeof(T) / 8); ++w) d[w] = ld_dev(s + w);
-  return v;
-}
-template <class T> __device__ __forceinline__ void zero_recs(T *dst, int n) {
-  uint64_t *d = (uint64_t *)dst;
-  const int words = n * (int)(sizeof(T) / 8);
-  for (int w = threadIdx.x; w < words; w += TPB) st_dev(d + w, (uint64_t)0);
-}
-
-template <int DT> __device__ __forceinline__ float load_elem(const char *row, int64_t x) {
-  if constexpr (DT == SV_BF16) {
-    return __uint_as_float((uint32_t)(*(const uint16_t *)(row + x * 2)) << 16);
-  } else {
-    return *(const float *)(row + x * 4);
-  }
-}
-
-// element w of a 16-byte vector
-template <int DT> __device__ __forceinline__ float unpack(const u32x4 &v, int w) {
-  if constexpr (DT == SV_BF16) {
-    const uint32_t word = v[w >> 1];
-    return __uint_as_float((w & 1) ? (word & 0xffff0000u) : (word << 16));
-  } else {
-    return __uint_as_float(v[w]);
-  }
-}
-
-// tile-local position of element w of this thread's vector s
-template <int DT> __device__ __forceinline__ int tpos(int s, int w) {
-  return s * (TPB * Fmt<DT>::W) + (int)threadIdx.x * Fmt<DT>::W + w;
-}
-
-// tile-local position of element w of this thread's vector s when each thread
-// owns NSEG consecutive vectors (the draw's order)
-template <int DT> __device__ __forceinline__ int dpos(int s, int w) {
-  return ((int)threadIdx.x * NSEG + s) * Fmt<DT>::W + w;
-}
-
-// Load one tile of a row into registers; entries past V read as -inf.
-// Streaming (TM false): vector s of a thread sits at tpos (vectors interleaved
-// over the threads) and the loads are marked nontemporal, since each logit is
-// read once.  Draw (TM true): vector s sits at dpos (each thread's vectors
-// consecutive) with ordinary loads, which measured faster for this re-read.
-template <int DT, bool TM = false>
-__device__ __forceinline__ void load_tile(const char *row, int c, int V, bool vec, u32x4 (&r)[NSEG]) {
-  constexpr int E = Fmt<DT>::E, W = Fmt<DT>::W;
-  const int64_t c0 = (int64_t)c * Fmt<DT>::TILE;
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    const int64_t e0 = c0 + (TM ? dpos<DT>(s, 0) : tpos<DT>(s, 0));
-    if (vec && e0 + W <= V) {
-      if (TM) r[s] = *(const u32x4 *)(row + e0 * E);
-      else r[s] = __builtin_nontemporal_load((const u32x4 *)(row + e0 * E));
-    } else {
-      u32x4 v;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (DT == SV_BF16) {
-          const int64_t x = e0 + 2 * q;
-          uint32_t lo = x < V ? *(const uint16_t *)(row + x * 2) : 0xff80u;
-          uint32_t hi = x + 1 < V ? *(const uint16_t *)(row + (x + 1) * 2) : 0xff80u;
-          v[q] = lo | (hi << 16);
-        } else {
-          const int64_t x = e0 + q;
-          v[q] = x < V ? *(const uint32_t *)(row + x * 4) : 0xff800000u;
-        }
-      }
-      r[s] = v;
-    }
-  }
-}
-
-template <int DT> __device__ __forceinline__ float thread_max(const u32x4 (&r)[NSEG]) {
-  float m = NEG_INF;
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s)
-#pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) m = fmaxf(m, unpack<DT>(r[s], w));
-  return m;
-}
-
-template <int DT> __device__ __forceinline__ bool thread_has_nan(const u32x4 (&r)[NSEG]) {
-  bool nan = false;
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s)
-#pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) { const float x = unpack<DT>(r[s], w); nan |= !(x == x); }
-  return nan;
-}
-
-// exp2((x - m) * sc) of one element; a thread whose slice is all -inf uses 0 as m
-__device__ __forceinline__ float scaled_exp(float x, float m, float sc) {
-  const float ms = (m == NEG_INF) ? 0.f : m;
-  return __builtin_amdgcn_exp2f((x - ms) * sc);
-}
-
-// Sequential fp32 sum of the thread's exp2((x - ref) * sc); flags NaN / +inf.
-template <int DT>
-__device__ __forceinline__ float thread_expsum(const u32x4 (&r)[NSEG], float ref, float sc, int &flags) {
-  float s = 0.f;
-#pragma unroll
-  for (int g = 0; g < NSEG; ++g)
-#pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) s += __builtin_amdgcn_exp2f((unpack<DT>(r[g], w) - ref) * sc);
-  flags = 0;
-  if (!(s == s)) flags = thread_has_nan<DT>(r) ? SV_STATUS_NAN : SV_STATUS_POSINF;
-  return s;
-}
-
-// s * exp2((m - M) * sc) in fp64: a partial sum relative to m, rescaled to M
-__device__ __forceinline__ double rescale(double s, float m, float M, float sc) {
-  return m == NEG_INF ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - M) * sc);
-}
-
-// Per-thread scale turning scaled exps into probabilities: exp2((m_thread - m_row) * sc) / s_row.
-__device__ __forceinline__ float prob_scale(float m_thr, float m_row, double s_row, float sc) {
-  if (m_thr == NEG_INF) return 0.f;
-  return (float)((double)__builtin_amdgcn_exp2f((m_thr - m_row) * sc) / s_row);
-}
-
-// Mass of one element: residual max(0, p - q) for a pair row, p for a single row.
-template <int DT>
-__device__ __forceinline__ float elem_mass(const u32x4 &vt, const u32x4 &vd, int w, bool resid, float mt, float md,
-                                           float at, float ad, float sc) {
-  const float p = scaled_exp(unpack<DT>(vt, w), mt, sc) * at;
-  if (!resid) return p;
-  const float q = scaled_exp(unpack<DT>(vd, w), md, sc) * ad;
-  const float r = p - q;
-  return r > 0.f ? r : 0.f;
-}
-
-// Sequential fp32 mass of each of the thread's vectors.
-template <int DT>
-__device__ __forceinline__ void seg_masses(const u32x4 (&rt)[NSEG], const u32x4 (&rd)[NSEG], bool resid, float mt,
-                                           float md, float at, float ad, float sc, float (&seg)[NSEG]) {
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    float a = 0.f;
-#pragma unroll
-    for (int w = 0; w < Fmt<DT>::W; ++w) a += elem_mass<DT>(rt[s], rd[s], w, resid, mt, md, at, ad, sc);
-    seg[s] = a;
-  }
-}
-
-// Exclusive prefix (fp64) of one value per thread over the workgroup, in
-// thread order: excl receives the sum over the threads before this one; returns
-// the total.  Fixed association: identical bits wherever it is evaluated.
-__device__ __forceinline__ double block_scan_d(double x, double &excl, Smem &sm) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const double inc = wave_scan_d(x);
-  const double prev = wave_prev_d(inc);
-  if (lane == 63) sm.d[0][wid] = inc;
-  __syncthreads();
-  double off = 0.0, tot = 0.0;
-  for (int w = 0; w < NWAVE; ++w) {
-    if (w < wid) off += sm.d[0][w];
-    tot += sm.d[0][w];
-  }
-  excl = off + prev;
-  __syncthreads();
-  return tot;
-}
-
 // Block-wide OR and MIN.
 __device__ __forceinline__ void block_or_min(int &o, int &m, Smem &sm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -1106,7 +764,7 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
 #pragma unroll
         for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rd[s], w, rmode, o1, o2, P.sc);
       mine = a;
-      const double t = block_scan_d((double)a, base, sm);
+      const double t = block_scan_d((double)a, base, sm.d[0]);
       if (tid == 0) st_dev(tot + 2 * c + round, tot_word(t));
       // the crossing tile, from the totals in tile order (wave 0, lane l
       // polling tile l's slot until every tile has published)
@@ -1175,7 +833,7 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
     }
   }
   // every draw workgroup of the sequence reports; the last clears its state
-  const int old = arrive(P.ddone + (int64_t)b * CTR, sm);
+  const int old = arrive(P.ddone + (int64_t)b * CTR, &sm.bc[7]);
   if (old != nT - 1) {
     if ((old < 0 || old >= nT) && tid == 0) atomicOr(P.fault, 2);
     return;

@@ -1,4 +1,5 @@
-"""ctypes wrapper of the plain-C fp64 oracle (sv_oracle.c).
+"""ctypes wrapper of the plain-C fp64 oracles: sv_oracle.c (verification) and
+kd_oracle.c (reward-weighted drafter distillation over the stored top-32).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  It shares no code with the HIP
@@ -14,6 +15,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sv_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "kd_oracle.c")]
 _LIB = os.path.join(_HERE, "libsv_oracle.so")
 
 STATUS_BAD_TOKEN, STATUS_NAN, STATUS_POSINF, STATUS_EMPTY_ROW, STATUS_BAD_UNIFORM = 1, 2, 4, 8, 16
@@ -24,7 +26,7 @@ def build() -> str:
     """Compile the oracle with gcc (plain C99, no fast-math, no FMA contraction)."""
     tmp = _LIB + ".tmp"
     subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-                           "-shared", "-o", tmp, _SRC, "-lm"])
+                           "-shared", "-o", tmp, *_SRCS, "-lm"])
     os.replace(tmp, _LIB)
     return _LIB
 
@@ -35,13 +37,16 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in _SRCS):
             build()
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         lib.orc_verify.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                    P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_verify.restype = ctypes.c_int
+        lib.kd_oracle.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_double, P, P, P, P, P, P, P, P, P, P]
+        lib.kd_oracle.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -92,3 +97,41 @@ def verify_workload(w, aux=True) -> OracleResult:
     """Oracle on an sv_inputs.Workload."""
     return verify(w.target, None if w.temperature == 0 else w.draft, w.draft_tokens,
                   None if w.temperature == 0 else w.uniforms, w.temperature, w.dtype, aux=aux)
+
+
+KD_BAD_INDEX, KD_NAN, KD_POSINF, KD_EMPTY = 1, 2, 4, 8
+
+
+def kd(logits, topk_val, topk_idx, row_sample, rewards, group, w_max=float("inf"), dtype=0, grad=True) -> OracleResult:
+    """Reward-weighted distillation oracle.  logits [N,V] float32, or uint16 bf16
+    bit patterns with dtype=1; topk_val [N,32] float32; topk_idx [N,32] int32;
+    row_sample [N] int32; rewards [S] float32.  Returns kl, weight, status
+    [N], loss (float) and, with grad, grad [N,V] (fp64)."""
+    lib = _load()
+    want = np.float32 if dtype == 0 else np.uint16
+    z = np.ascontiguousarray(logits)
+    assert z.dtype == want and z.ndim == 2
+    N, V = z.shape
+    tv = np.ascontiguousarray(topk_val, dtype=np.float32).reshape(N, TOPK)
+    ti = np.ascontiguousarray(topk_idx, dtype=np.int32).reshape(N, TOPK)
+    rs = np.ascontiguousarray(row_sample, dtype=np.int32).reshape(N)
+    rw = np.ascontiguousarray(rewards, dtype=np.float32).reshape(-1)
+    r = OracleResult(kl=np.empty(N), weight=np.empty(N), status=np.empty(N, np.int32),
+                     grad=np.empty((N, V)) if grad else None)
+    loss = np.zeros(1)
+    rc = lib.kd_oracle(N, V, int(dtype), V, rw.size, int(group), float(w_max), _ptr(z), _ptr(tv), _ptr(ti), _ptr(rs),
+                       _ptr(rw), _ptr(r["kl"]), _ptr(r["weight"]), _ptr(r["status"]), _ptr(loss), _ptr(r["grad"]))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    r["loss"] = float(loss[0])
+    return r
+
+
+def kd_workload(w, grad=True, rows=None) -> OracleResult:
+    """KD oracle on an sv_inputs.KDWorkload (optionally on a subset of its rows;
+    each row's weight still comes from its own sample's group)."""
+    z = w.logits if rows is None else w.logits[rows]
+    tv = w.topk_val if rows is None else w.topk_val[rows]
+    ti = w.topk_idx if rows is None else w.topk_idx[rows]
+    rs = w.row_sample if rows is None else w.row_sample[rows]
+    return kd(z, tv, ti, rs, w.rewards, w.group, w.w_max, w.dtype, grad=grad)

@@ -211,3 +211,78 @@ def fixed_rows(B: int, target_rows: np.ndarray, draft_rows: np.ndarray, T: float
     draft = np.broadcast_to(dr, (B, k, V)).copy()
     uniforms = _uniform24(_rng(seed, _T_UNIFORM, 0), (B, K1 + 1))
     return Workload("fixed", B, k, V, dtype, float(T), target, draft, tokens, uniforms, seed)
+
+
+# ---------------------------------------------------------------- distillation
+# Inputs of the reward-weighted drafter distillation over stored top-32 soft
+# targets.  Rows are stored positions of rollout samples (L positions per
+# sample, samples in groups of `group` rollouts of one prompt).  Per row: 32
+# distinct token ids with stored target logits ~ N(10, 2^2) (bf16-representable
+# values), and drafter logits ~ N(0, 3^2) except at the stored ids, where they
+# are the stored value plus N(0, 1.5^2).  Rewards take the levels of the pages'
+# GRPO example, {0, 0.3, 0.8, 1.0}, uniformly.
+_T_KD_LOGITS, _T_KD_IDS, _T_KD_VALS, _T_KD_NOISE, _T_KD_REWARD = 10, 11, 12, 13, 14
+KD_TOP = 32
+
+
+@dataclasses.dataclass
+class KDWorkload:
+    name: str
+    N: int
+    V: int
+    dtype: int             # of the drafter logits
+    group: int
+    L: int                 # stored positions per sample
+    logits: np.ndarray     # [N,V] float32, or uint16 bf16 patterns
+    topk_val: np.ndarray   # [N,32] float32
+    topk_idx: np.ndarray   # [N,32] int32
+    row_sample: np.ndarray  # [N] int32
+    rewards: np.ndarray    # [S] float32
+    w_max: float = float("inf")
+    seed: int = 0
+
+    @property
+    def S(self) -> int:
+        return int(self.rewards.size)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == F32 else 2
+
+    def alg_bytes(self, grad_bytes: int = 0) -> int:
+        """Drafter logit bytes read once, plus the gradient written once."""
+        return self.N * self.V * (self.elem_bytes + grad_bytes)
+
+
+def kd_workload(name: str, samples: int, group: int, L: int, V: int, dtype: int, seed: int,
+                w_max: float = float("inf")) -> KDWorkload:
+    N = samples * L
+    store = np.float32 if dtype == F32 else np.uint16
+    logits = np.empty((N, V), dtype=store)
+    tv = np.empty((N, KD_TOP), np.float32)
+    ti = np.empty((N, KD_TOP), np.int32)
+    for n in range(N):
+        ids = _rng(seed, _T_KD_IDS, n).choice(V, size=min(KD_TOP, V), replace=False).astype(np.int32)
+        vals = bf16_to_f32(bf16_round(_rng(seed, _T_KD_VALS, n).standard_normal(ids.size).astype(np.float32) * 2 + 10))
+        z = (_rng(seed, _T_KD_LOGITS, n).standard_normal(V) * 3.0).astype(np.float32)
+        z[ids] = vals + (_rng(seed, _T_KD_NOISE, n).standard_normal(ids.size) * 1.5).astype(np.float32)
+        logits[n] = z if dtype == F32 else bf16_round(z)
+        tv[n] = -np.inf
+        ti[n] = -1
+        tv[n, :ids.size] = vals
+        ti[n, :ids.size] = ids
+    levels = np.array([0.0, 0.3, 0.8, 1.0], np.float32)
+    rewards = levels[_rng(seed, _T_KD_REWARD, 0).integers(0, 4, size=samples)]
+    row_sample = (np.arange(N) // L).astype(np.int32)
+    return KDWorkload(name, N, V, dtype, group, L, logits, tv, ti, row_sample, rewards, float(w_max), seed)
+
+
+def kd_small(seed: int = 1101, V: int = 20000, dtype: int = BF16) -> KDWorkload:
+    """3 groups of 4 samples, 2 positions each: 24 rows, a ragged last tile."""
+    return kd_workload("kd_small", 12, 4, 2, V, dtype, seed)
+
+
+def kd_rollout(seed: int = 1106, prompts: int = 32, rollouts: int = 8, L: int = 16, V: int = 151936) -> KDWorkload:
+    """The distillation batch of one GRPO step: 32 prompts x 8 rollouts, 16
+    stored positions each (4096 rows), V = 151936, bf16 drafter logits."""
+    return kd_workload("kd_rollout", prompts * rollouts, rollouts, L, V, BF16, seed)

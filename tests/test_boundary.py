@@ -15,7 +15,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = sv.declared_functions()
-    assert set(names) == {"spec_verify", "spec_verify_workspace_bytes", "spec_verify_error_string"}
+    assert set(names) == {"spec_verify", "spec_verify_workspace_bytes", "spec_verify_error_string",
+                          "sv_kd", "sv_kd_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -80,6 +81,49 @@ def test_host_validation_codes():
     assert _call(sv.make_shape(0, 3, 1000, 0, 1.0)) == sv.SV_OK
 
 
+def test_kd_workspace_bytes():
+    f = sv.sv_kd_workspace_bytes
+    small = f(sv.make_kd_shape(24, 20000, sv.SV_BF16, sv.SV_F32, 12, 4))
+    big = f(sv.make_kd_shape(4096, 151936, sv.SV_BF16, sv.SV_BF16, 256, 8))
+    assert 0 < small < big < 16 << 20
+    assert f(sv.make_kd_shape(-1, 100, 0, 0, 1, 1)) == 0
+    assert f(sv.make_kd_shape(1, 0, 0, 0, 1, 1)) == 0
+    assert f(sv.make_kd_shape(1, 100, 0, 0, 3, 2)) == 0          # group must divide S
+    assert f(sv.make_kd_shape(1, 100, 0, 0, 2, 2, w_max=0.0)) == 0
+    assert f(sv.make_kd_shape(1, 262144, sv.SV_F32, 0, 1, 1)) > 0
+    assert f(sv.make_kd_shape(1, 262145, sv.SV_F32, 0, 1, 1)) == 0
+    assert f(sv.make_kd_shape(1, 524288, sv.SV_BF16, 0, 1, 1)) > 0
+    assert f(sv.make_kd_shape(1, 524289, sv.SV_BF16, 0, 1, 1)) == 0
+
+
+def _kd_call(shape, **over):
+    a = dict(z=FAKE, tv=FAKE, ti=FAKE, rs=FAKE, rw=FAKE, kl=FAKE, w=None, st=None, loss=FAKE, g=None,
+             ws=FAKE * 16, wsb=1 << 30)
+    a.update(over)
+    return sv.sv_kd(shape, a["z"], a["tv"], a["ti"], a["rs"], a["rw"], a["kl"], a["w"], a["st"], a["loss"], a["g"],
+                    a["ws"], a["wsb"], None)
+
+
+def test_kd_host_validation_codes():
+    good = sv.make_kd_shape(24, 20000, sv.SV_BF16, sv.SV_F32, 12, 4)
+    assert sv.sv_kd(None, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == sv.SV_ERR_NULL
+    assert _kd_call(sv.make_kd_shape(24, 20000, 5, 0, 12, 4)) == sv.SV_ERR_DTYPE
+    assert _kd_call(sv.make_kd_shape(24, 20000, 0, 9, 12, 4)) == sv.SV_ERR_DTYPE
+    assert _kd_call(sv.make_kd_shape(-1, 20000, 0, 0, 12, 4)) == sv.SV_ERR_SHAPE
+    assert _kd_call(sv.make_kd_shape(24, 0, 0, 0, 12, 4)) == sv.SV_ERR_SHAPE
+    assert _kd_call(sv.make_kd_shape(24, 20000, 0, 0, 12, 5)) == sv.SV_ERR_SHAPE
+    assert _kd_call(sv.make_kd_shape(24, 20000, 0, 0, 0, 1)) == sv.SV_ERR_SHAPE
+    assert _kd_call(sv.make_kd_shape(24, 20000, 0, 0, 12, 4, w_max=float("nan"))) == sv.SV_ERR_SHAPE
+    assert _kd_call(sv.make_kd_shape(24, 20000, 0, 0, 12, 4, row_stride=19999)) == sv.SV_ERR_SHAPE
+    for k in ("z", "tv", "ti", "rs", "rw", "kl", "loss"):
+        assert _kd_call(good, **{k: None}) == sv.SV_ERR_NULL, k
+    assert _kd_call(good, ws=None) == sv.SV_ERR_WORKSPACE
+    need = sv.sv_kd_workspace_bytes(good)
+    assert _kd_call(good, wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    assert _kd_call(good, ws=FAKE * 16 + 8) == sv.SV_ERR_WORKSPACE
+    assert _kd_call(sv.make_kd_shape(0, 20000, 0, 0, 12, 4)) == sv.SV_OK
+
+
 def test_product_path_never_touches_the_oracle():
     """Neither the binding nor the HIP source names the oracle package."""
     import glob
@@ -88,3 +132,4 @@ def test_product_path_never_touches_the_oracle():
     for f in glob.glob(os.path.join(pkg, "*.py")) + glob.glob(os.path.join(pkg, "csrc", "*")):
         text = open(f).read()
         assert "import oracle" not in text and "sv_oracle" not in text and "orc_verify" not in text, f
+        assert "kd_oracle" not in text, f
