@@ -16,6 +16,7 @@ the plain C oracle on the host over a bounded number of whole batches.
   python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|tiny]
   python bench.py --workload kd   # the drafter distillation step over the stored top-32 (its own metric)
   python bench.py --copy-calib    # a plain 1 GiB device copy, for HBM counter calibration
+  python bench.py --source-hash sv_verify|sv_kd_kernel   # the source hash a profile summary records
 """
 import argparse
 import json
@@ -55,20 +56,33 @@ def describe(w):
     return f"{w.name} B={w.B} k={w.k} V={w.V} {'bf16' if w.dtype else 'f32'} T={w.temperature:g}"
 
 
-def counted_traffic(w):
-    """HBM bytes per sv_verify launch from the committed rocprofv3 counter
-    summary of this workload (fetched + written, copy-calibrated), or None when
-    there is none or the kernel source changed since the counters were taken."""
+KERNEL_SOURCES = {
+    "sv_verify": ["draft_verification_spec_amd/csrc/spec_verify.hip", "draft_verification_spec_amd/csrc/sv_device.h"],
+    "sv_kd_kernel": ["draft_verification_spec_amd/csrc/sv_kd.hip", "draft_verification_spec_amd/csrc/sv_device.h"],
+}
+
+
+def source_hash(kernel):
+    """sha256 over the kernel's source files, in order."""
     import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def counted_traffic(kernel, profile_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/<profile_name>.md (fetched + written, copy-calibrated), or None
+    when there is none or the kernel's sources changed since the counters were
+    taken."""
     import re
-    name = f"sv_verify_{w.name}_B{w.B}_k{w.k}_V{w.V}_{'bf16' if w.dtype else 'f32'}.md"
-    path = os.path.join(ROOT, "profiles", name)
-    src = os.path.join(ROOT, "draft_verification_spec_amd", "csrc", "spec_verify.hip")
+    path = os.path.join(ROOT, "profiles", profile_name + ".md")
     if not os.path.exists(path):
         return None
     m = re.search(r"traffic_per_launch: source_sha256=([0-9a-f]{64}) fetch_bytes=(\d+) write_bytes=(\d+)",
                   open(path).read())
-    if not m or hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(1):
+    if not m or source_hash(kernel) != m.group(1):
         return None
     return int(m.group(2)) + int(m.group(3))
 
@@ -168,7 +182,9 @@ def bench_kd(args):
         "rows_per_s": round(w.N / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "sv_kd_kernel",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic("sv_kd_kernel", f"sv_kd_kernel_{w.name}_N{w.N}_V{w.V}_bf16"),
+                     "kernel": "sv_kd_kernel",
                      "kernel_us_mean": round(kern_avg * 1e3, 3),
                      "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, q)) * 1e3, 3) for q in (10, 50, 90)]},
         "loss": float(loss.cpu()[0]),
@@ -176,19 +192,25 @@ def bench_kd(args):
     if not args.no_cpu:
         import oracle
         oracle.build()
-        rows = np.arange(w.N)                   # the whole batch: a few seconds of oracle work
+        rows = np.arange(w.N)                   # the whole batch, 256 rows at a time (bounded memory)
         t1 = time.perf_counter()
-        o = oracle.kd_workload(w, grad=True, rows=rows)
+        o_kl, o_status = [], []
+        for i in range(0, w.N, 256):
+            q = oracle.kd_workload(w, grad=True, rows=rows[i:i + 256])
+            o_kl.append(q.kl)
+            o_status.append(q.status)
+            del q
         dt = time.perf_counter() - t1
+        o_kl, o_status = np.concatenate(o_kl), np.concatenate(o_status)
         sample_bytes = len(rows) * w.V * (w.elem_bytes + 2)
         g_kl = kl.cpu().numpy()[rows]
-        ok = o.status == 0
+        ok = o_status == 0
         line["cpu_baseline"] = {
             "value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"all {len(rows)} rows of the batch (loss and fp64 gradient), {dt:.2f} s, single thread of "
                       f"{os.cpu_count()} host threads", "rows_per_s": round(len(rows) / dt, 2)}
-        line["parity_vs_oracle"] = {"rows": int(len(rows)), "max_abs_kl_err": float(np.max(np.abs(g_kl[ok] - o.kl[ok]))),
-                                    "status_equal": bool(np.array_equal(st.cpu().numpy()[rows], o.status))}
+        line["parity_vs_oracle"] = {"rows": int(len(rows)), "max_abs_kl_err": float(np.max(np.abs(g_kl[ok] - o_kl[ok]))),
+                                    "status_equal": bool(np.array_equal(st.cpu().numpy()[rows], o_status))}
     print(json.dumps(line), flush=True)
 
 
@@ -201,11 +223,15 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: enough for 4x the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--source-hash", default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the verification step runs on a single MI355X "
               "(sharding over B or V is a design note only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.source_hash:
+        print(source_hash(args.source_hash))
+        return
     if args.copy_calib:
         return copy_calib()
     if args.workload in ("kd", "kd_small"):
@@ -272,7 +298,9 @@ def main():
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(w),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic("sv_verify", f"sv_verify_{w.name}_B{w.B}_k{w.k}_V{w.V}_"
+                                                             f"{'bf16' if w.dtype else 'f32'}"),
                      "kernel": "sv_verify", "kernel_us_mean": round(kern_avg * 1e3, 3),
                      "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, q)) * 1e3, 3) for q in (10, 50, 90)]},
         "mean_accepted_len": float(np.mean(g["accepted_len"])),
