@@ -13,7 +13,7 @@ merges, assembly and draw; HIP events the library records right before and
 after it on the launch stream), against the 8 TB/s HBM peak.  cpu_baseline =
 the plain C oracle on the host over a bounded number of whole batches.
 
-  python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|tiny]
+  python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|plain|tiny]
   python bench.py --workload kd   # the drafter distillation step over the stored top-32 (its own metric)
   python bench.py --copy-calib    # a plain 1 GiB device copy, for HBM counter calibration
   python bench.py --source-hash sv_verify|sv_kd_kernel   # the source hash a profile summary records
@@ -49,6 +49,8 @@ def make_workload(name):
         return sv_inputs.wide(greedy=True)
     if name == "tiny":
         return sv_inputs.tiny()
+    if name == "plain":
+        return sv_inputs.plain()
     raise SystemExit(f"unknown workload {name}")
 
 

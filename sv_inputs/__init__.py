@@ -25,6 +25,8 @@ Workloads follow the five configurations the verification step is measured on:
             shared by the 8 rollouts of a prompt
   wide      B=32, k=15, V=151936, fp32, t~N(0,3^2), d=t+N(0,2^2), T=1
             (and T=0 greedy with draft tokens = argmax of the draft row)
+  plain     B=32, k=0, V=151936, bf16, as steady: one token sampled per sequence
+and the distillation batches (kd_workload, kd_small, kd_rollout) below.
 """
 from __future__ import annotations
 
@@ -275,6 +277,12 @@ def kd_workload(name: str, samples: int, group: int, L: int, V: int, dtype: int,
     rewards = levels[_rng(seed, _T_KD_REWARD, 0).integers(0, 4, size=samples)]
     row_sample = (np.arange(N) // L).astype(np.int32)
     return KDWorkload(name, N, V, dtype, group, L, logits, tv, ti, row_sample, rewards, float(w_max), seed)
+
+
+def plain(seed: int = 1007, B: int = 32, V: int = 151936) -> Workload:
+    """k = 0: plain temperature sampling of one token per sequence (the engine's
+    non-speculative step), steady-state logits."""
+    return make_workload("plain", B, 0, V, BF16, 1.0, seed, 3.0, 1.0, peaks=20, peak_boost=8.0)
 
 
 def kd_small(seed: int = 1101, V: int = 20000, dtype: int = BF16) -> KDWorkload:

@@ -192,9 +192,16 @@ def test_k_zero(sv, orc, T):
     check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
 
 
+def test_plain_full_vocabulary(sv, orc):
+    """k = 0 at the pages' vocabulary: plain temperature sampling (bonus draws
+    only) with the top-32, in the plain bench workload's distribution."""
+    w = sv_inputs.plain(B=8)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+
+
 @pytest.mark.parametrize("dtype,V", [(sv_inputs.BF16, 128 * 4096), (sv_inputs.F32, 128 * 2048)])
 def test_largest_vocab(sv, orc, dtype, V):
-    """The largest vocabulary the library takes: 128 tiles per row."""
+    """The largest vocabulary the library takes: 64 tiles of 16 KB per row."""
     w = sv_inputs.make_workload("maxV", 1, 1, V, dtype, 1.0, 1601, 3.0, 1.0)
     check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
 
