@@ -37,9 +37,11 @@
 //             the totals in tile order, and the one that holds it draws the
 //             token from its registers.
 //
-// A streaming workgroup only ever waits for workgroups of a lower index, which
-// the hardware dispatches first; a draw workgroup for streaming workgroups and
-// for the other draw workgroups of its sequence, dispatched with it.  Every
+// A streaming workgroup only ever waits for workgroups of lower items, which
+// its XCD dispatches first (items run in order within an XCD; a group or a
+// sequence that spans two XCDs waits across the boundary, a handful of
+// workgroups at most); a draw workgroup waits for streaming workgroups and for
+// the other draw workgroups of its sequence, dispatched with it.  Every
 // wait is bounded in time: a wait that gives up sets the fault word (reported
 // as SV_STATUS_SYNC_TIMEOUT) and the kernel still finishes.  Data moves
 // between workgroups through the workspace with device-scope write-through
@@ -291,6 +293,17 @@ struct Geo {
   bool pair;
   const char *trow, *drow;
 };
+
+// Streaming item of workgroup bid.  The chip deals workgroups to its 8 XCDs
+// round-robin (bid mod 8), each XCD dispatching its share in order; items are
+// laid out so that XCD x takes one contiguous run of them, in order.  A
+// group's tiles then sit on one XCD and its last tile is dispatched after the
+// others (on a run boundary the group spans two XCDs), instead of being spread
+// over all eight, whose progress differs.
+__device__ __forceinline__ int xcd_item(int bid, int n) {
+  const int x = bid & 7, q = bid >> 3, base = n >> 3, rem = n & 7;
+  return x * base + (x < rem ? x : rem) + q;
+}
 
 template <int DT, bool GREEDY> __device__ __forceinline__ Geo geo(const Params &P, int item) {
   Geo G;
@@ -853,12 +866,12 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(Fmt<DT>::WA
   constexpr int W = Fmt<DT>::W, TILE = Fmt<DT>::TILE;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int V = P.V;
-  const int item = blockIdx.x;
-  if (!GREEDY && item >= P.items) {                      // draw workgroups come last
-    const int d = item - P.items;
+  if (!GREEDY && (int)blockIdx.x >= P.items) {           // draw workgroups come last
+    const int d = blockIdx.x - P.items;
     draw_tile<DT>(P, d / P.nT, d - (d / P.nT) * P.nT, sm);
     return;
   }
+  const int item = xcd_item(blockIdx.x, P.items);
   const Geo G = geo<DT, GREEDY>(P, item);
   const int c = G.c;
   const bool pair = G.pair;
