@@ -294,17 +294,6 @@ struct Geo {
   const char *trow, *drow;
 };
 
-// Streaming item of workgroup bid.  The chip deals workgroups to its 8 XCDs
-// round-robin (bid mod 8), each XCD dispatching its share in order; items are
-// laid out so that XCD x takes one contiguous run of them, in order.  A
-// group's tiles then sit on one XCD and its last tile is dispatched after the
-// others (on a run boundary the group spans two XCDs), instead of being spread
-// over all eight, whose progress differs.
-__device__ __forceinline__ int xcd_item(int bid, int n) {
-  const int x = bid & 7, q = bid >> 3, base = n >> 3, rem = n & 7;
-  return x * base + (x < rem ? x : rem) + q;
-}
-
 template <int DT, bool GREEDY> __device__ __forceinline__ Geo geo(const Params &P, int item) {
   Geo G;
   const int K1 = P.k + 1;

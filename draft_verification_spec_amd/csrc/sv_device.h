@@ -291,4 +291,15 @@ __device__ __forceinline__ double block_scan_d(double x, double &excl, double *p
   return tot;
 }
 
+// Work item of workgroup bid in a launch of n items.  The chip deals
+// workgroups to its 8 XCDs round-robin (bid mod 8), each XCD dispatching its
+// share in order; items are laid out so that XCD x takes one contiguous run of
+// them, in order.  The tiles of one row (or group) then sit on one XCD and are
+// dispatched together (a row on a run boundary spans two XCDs), instead of
+// being spread over all eight, whose progress differs.
+__device__ __forceinline__ int xcd_item(int bid, int n) {
+  const int x = bid & 7, q = bid >> 3, base = n >> 3, rem = n & 7;
+  return x * base + (x < rem ? x : rem) + q;
+}
+
 }  // namespace sv_dev
