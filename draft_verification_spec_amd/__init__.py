@@ -37,7 +37,10 @@ class sv_shape_t(ctypes.Structure):
 class sv_aux_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_void_p), ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p),
                 ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p),
-                ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p)]
+                ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p), ("item_layout", ctypes.c_int32)]
+
+
+SV_LAYOUT_AUTO, SV_LAYOUT_LAUNCH, SV_LAYOUT_XCD_RUNS = 0, 1, 2
 
 
 class sv_kd_shape_t(ctypes.Structure):
@@ -68,6 +71,8 @@ def load_library() -> ctypes.CDLL:
         P = ctypes.c_void_p
         lib.spec_verify_workspace_bytes.argtypes = [ctypes.POINTER(sv_shape_t)]
         lib.spec_verify_workspace_bytes.restype = ctypes.c_size_t
+        lib.spec_verify_layout_choice.argtypes = [ctypes.POINTER(sv_shape_t)]
+        lib.spec_verify_layout_choice.restype = ctypes.c_int
         lib.spec_verify_error_string.argtypes = [ctypes.c_int]
         lib.spec_verify_error_string.restype = ctypes.c_char_p
         lib.spec_verify.argtypes = [ctypes.POINTER(sv_shape_t), P, P, P, P, P, P, P, P,
@@ -97,6 +102,10 @@ def make_shape(B, k, V, dtype, temperature, target_row_stride=0, draft_row_strid
 
 def spec_verify_workspace_bytes(shape: sv_shape_t) -> int:
     return int(load_library().spec_verify_workspace_bytes(ctypes.byref(shape)))
+
+
+def spec_verify_layout_choice(shape: sv_shape_t) -> int:
+    return int(load_library().spec_verify_layout_choice(ctypes.byref(shape)))
 
 
 def spec_verify_error_string(code: int) -> str:
@@ -145,14 +154,15 @@ def _row_stride(t, rows_per_seq):
 
 
 def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bool = False,
-           workspace=None, stream=None, events=None) -> Result:
+           workspace=None, stream=None, events=None, layout: int = SV_LAYOUT_AUTO) -> Result:
     """Verify on torch tensors of one device.
 
     target [B,k+1,V] and draft [B,k,V] (float32 or bfloat16, same dtype; draft
     may be None when temperature == 0), draft_tokens [B,k] int32, uniforms
     [B,k+2] float32 (None allowed when temperature == 0).  events: optional
-    pair of torch.cuda.Event recorded right before and after the streaming
-    kernel on the launch stream.  Returns device tensors.
+    pair of torch.cuda.Event recorded right before and after the kernel on
+    the launch stream.  layout: SV_LAYOUT_* order of the streaming items
+    (results do not depend on it).  Returns device tensors.
     """
     import torch
     if target.dim() != 3:
@@ -197,14 +207,15 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bo
     tv = torch.empty(B, K1, TOPK, **f32)
     ti = torch.empty(B, K1, TOPK, **i32)
     st = torch.empty(B, **i32)
-    a = sv_aux_t(st.data_ptr(), None, None, None, None, None, None)
+    a = sv_aux_t(st.data_ptr(), None, None, None, None, None, None, int(layout))
     lt = ld = pt = qt = None
     if aux and not greedy:
         lt = torch.empty(B, K1, **f32)
         ld = torch.empty(B, k, **f32)
         pt = torch.empty(B, k, **f32)
         qt = torch.empty(B, k, **f32)
-        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr(), None, None)
+        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr(), None, None,
+                     int(layout))
     if events is not None:
         a.event_begin, a.event_end = events[0].cuda_event, events[1].cuda_event
     nbytes = spec_verify_workspace_bytes(shape)

@@ -63,6 +63,7 @@
 
 #include "spec_verify.h"
 #include "sv_device.h"
+#include "sv_dispatch.h"
 
 namespace {
 
@@ -120,6 +121,7 @@ struct Params {
                                        // tot_word: 0 until published
   int32_t B, k, V, nT;
   int32_t items;                       // streaming workgroups: B * (k + 1) * nT
+  int32_t xcd_runs;                    // 1: one contiguous run of items per XCD; 0: launch order
   float T, sc;                         // sc = log2(e) / T
   double scd;
   int32_t t_vec, d_vec;                // rows 16-byte aligned
@@ -860,7 +862,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(Fmt<DT>::WA
     draw_tile<DT>(P, d / P.nT, d - (d / P.nT) * P.nT, sm);
     return;
   }
-  const int item = xcd_item(blockIdx.x, P.items);
+  const int item = P.xcd_runs ? xcd_item(blockIdx.x, P.items) : (int)blockIdx.x;
   const Geo G = geo<DT, GREEDY>(P, item);
   const int c = G.c;
   const bool pair = G.pair;
@@ -1039,7 +1041,34 @@ hipError_t launch(const Params &P, bool greedy, hipStream_t stream, hipEvent_t e
   return hipSuccess;
 }
 
+// The item layout for a shape.  In launch order, tile c of every group goes
+// to XCD (g * nT + c) mod 8, so with a tile count divisible by 4 the groups'
+// last tiles, which run the merges, crowd onto 2 or 1 of the 8 XCDs (a 16-tile
+// row measured 1.4x slower): XCD runs then.  Otherwise the measured table
+// (taken at 19 bf16 and 38 fp32 tiles): the entry of the same dtype and mode
+// nearest in (log2 B, log2(k + 1)); XCD runs where there is none.
+int table_layout(const sv_shape_t *s) {
+  const int nT = (s->V + tile_of(s->dtype) - 1) / tile_of(s->dtype);
+  if (nT % 4 == 0) return SV_LAYOUT_XCD_RUNS;
+  const bool greedy = s->temperature == 0.f;
+  double best = 1e30;
+  int layout = SV_LAYOUT_XCD_RUNS;
+  for (const SvLayoutEntry *e = kSvLayoutTable; e->dtype >= 0; ++e) {
+    if (e->dtype != s->dtype || e->greedy != (greedy ? 1 : 0)) continue;
+    const double db = log2((double)(s->B > 0 ? s->B : 1)) - log2((double)e->B);
+    const double dk = log2((double)s->k + 1.0) - log2((double)e->k + 1.0);
+    const double d = db * db + dk * dk;
+    if (d < best) { best = d; layout = e->layout; }
+  }
+  return layout;
+}
+
 }  // namespace
+
+extern "C" int spec_verify_layout_choice(const sv_shape_t *s) {
+  if (!s || !shape_ok(s) || !(s->temperature >= 0.f) || s->temperature == __builtin_inff()) return 0;
+  return table_layout(s);
+}
 
 extern "C" size_t spec_verify_workspace_bytes(const sv_shape_t *s) {
   if (!s || !shape_ok(s)) return 0;
@@ -1079,6 +1108,9 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   if (items + (int64_t)s.B * nT > 0x7fffffffLL || (int64_t)s.B * (s.k + 2) > 0x7fffffffLL) return SV_ERR_SHAPE;
   if (!(s.temperature >= 0.f) || s.temperature == __builtin_inff()) return SV_ERR_TEMPERATURE;
   const bool greedy = s.temperature == 0.f;
+  const int req_layout = aux ? aux->item_layout : SV_LAYOUT_AUTO;
+  if (req_layout != SV_LAYOUT_AUTO && req_layout != SV_LAYOUT_LAUNCH && req_layout != SV_LAYOUT_XCD_RUNS)
+    return SV_ERR_SHAPE;
   if (s.B == 0) return SV_OK;
   if (!target_logits || !accepted_len || !out_tokens || !topk_val || !topk_idx) return SV_ERR_NULL;
   if (s.k > 0 && !draft_tokens) return SV_ERR_NULL;
@@ -1119,6 +1151,7 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   P.V = s.V;
   P.nT = (int32_t)nT;
   P.items = (int32_t)items;
+  P.xcd_runs = (req_layout == SV_LAYOUT_AUTO ? table_layout(&s) : req_layout) == SV_LAYOUT_XCD_RUNS ? 1 : 0;
   P.T = greedy ? 0.f : s.temperature;
   P.scd = greedy ? 0.0 : 1.4426950408889634 / (double)s.temperature;
   P.sc = (float)P.scd;

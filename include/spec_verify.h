@@ -52,7 +52,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
 #define SV_OK 0
 #define SV_ERR_NULL (-1)        /* a required pointer is NULL */
 #define SV_ERR_SHAPE (-2)       /* B < 0, k < 0, V < 1, V above the maximum (524288 for bf16,
-                                   262144 for fp32), a row stride < V, or sizes too large */
+                                   262144 for fp32), a row stride < V, sizes too large, or an
+                                   unknown aux->item_layout */
 #define SV_ERR_TEMPERATURE (-3) /* temperature < 0, NaN or infinite */
 #define SV_ERR_DTYPE (-4)       /* dtype not SV_F32 / SV_BF16 */
 #define SV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than spec_verify_workspace_bytes */
@@ -89,10 +90,27 @@ typedef struct {
     void *event_begin;   /* hipEvent_t recorded on the stream right before the kernel
                             launch, or NULL */
     void *event_end;     /* hipEvent_t recorded right after it, or NULL */
+    int32_t item_layout; /* order in which the streaming workgroups take the (group, tile)
+                            items: SV_LAYOUT_AUTO (0, the library's measured table),
+                            SV_LAYOUT_LAUNCH (launch order) or SV_LAYOUT_XCD_RUNS (one
+                            contiguous run of items per XCD); results are identical */
 } sv_aux_t;
+
+#define SV_LAYOUT_AUTO 0
+#define SV_LAYOUT_LAUNCH 1
+#define SV_LAYOUT_XCD_RUNS 2
 
 /* Bytes of device workspace one call with this shape needs. */
 size_t spec_verify_workspace_bytes(const sv_shape_t *shape);
+
+/* The item layout (SV_LAYOUT_LAUNCH or SV_LAYOUT_XCD_RUNS) that SV_LAYOUT_AUTO
+ * takes for this shape: SV_LAYOUT_XCD_RUNS when a row's number of 16 KB tiles
+ * is divisible by 4 (launch order would crowd the merges onto one or two
+ * XCDs); else the
+ * faster one in a table measured on MI355X at V = 151936 over batch sizes
+ * 1..256, draft lengths 0..15, both dtypes and both modes (the entry nearest
+ * in log B and k).  Returns 0 for an invalid shape. */
+int spec_verify_layout_choice(const sv_shape_t *shape);
 
 /*
  * Enqueue one verification step on `stream` (a hipStream_t; NULL = default

@@ -16,7 +16,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = sv.declared_functions()
     assert set(names) == {"spec_verify", "spec_verify_workspace_bytes", "spec_verify_error_string",
-                          "sv_kd", "sv_kd_workspace_bytes"}
+                          "spec_verify_layout_choice", "sv_kd", "sv_kd_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -46,12 +46,25 @@ def test_workspace_bytes():
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
-def _call(shape, **over):
+def _call(shape, aux=None, **over):
     a = dict(t=FAKE, d=FAKE, x=FAKE, u=FAKE, acc=FAKE, out=FAKE, tv=FAKE, ti=FAKE, ws=FAKE * 16,
              wsb=1 << 30)
     a.update(over)
-    return sv.spec_verify(shape, a["t"], a["d"], a["x"], a["u"], a["acc"], a["out"], a["tv"], a["ti"], None,
+    return sv.spec_verify(shape, a["t"], a["d"], a["x"], a["u"], a["acc"], a["out"], a["tv"], a["ti"], aux,
                           a["ws"], a["wsb"], None)
+
+
+def test_layout_choice():
+    f = sv.spec_verify_layout_choice
+    for B in (1, 4, 32, 256):
+        for k in (0, 3, 15):
+            for dt in (sv.SV_F32, sv.SV_BF16):
+                for T in (0.0, 1.0):
+                    assert f(sv.make_shape(B, k, 151936, dt, T)) in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS)
+    assert f(sv.make_shape(-1, 3, 1000, 0, 1.0)) == 0
+    assert f(sv.make_shape(2, 3, 1000, 0, -1.0)) == 0
+    bad = sv.sv_aux_t(None, None, None, None, None, None, None, 3)
+    assert _call(sv.make_shape(2, 3, 1000, 0, 1.0), aux=bad) == sv.SV_ERR_SHAPE
 
 
 def test_host_validation_codes():

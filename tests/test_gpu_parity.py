@@ -192,6 +192,24 @@ def test_k_zero(sv, orc, T):
     check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
 
 
+@pytest.mark.parametrize("which", ["steady", "greedy"])
+def test_layouts_give_identical_results(sv, which):
+    """The two item layouts only reorder which workgroup takes which item."""
+    w = sv_inputs.make_workload("lay", 6, 3, 40000, sv_inputs.BF16, 0.0 if which == "greedy" else 1.0, 1801, 3.0, 1.0)
+    t, d, x, u = sv.to_device(w)
+    greedy = w.temperature == 0
+    res = []
+    for layout in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS, sv.SV_LAYOUT_AUTO):
+        log(f"spec_verify layouts {which} layout={layout}")
+        r = sv.verify(t, None if greedy else d, x, None if greedy else u, w.temperature, aux=not greedy, layout=layout)
+        torch.cuda.synchronize()
+        res.append(gpu_to_numpy(r))
+    for other in res[1:]:
+        for key, v in res[0].items():
+            if v is not None:
+                np.testing.assert_array_equal(v, other[key], err_msg=key)
+
+
 def test_plain_full_vocabulary(sv, orc):
     """k = 0 at the pages' vocabulary: plain temperature sampling (bonus draws
     only) with the top-32, in the plain bench workload's distribution."""
