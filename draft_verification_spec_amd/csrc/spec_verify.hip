@@ -796,48 +796,54 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
       rmode = false;                   // no residual mass left: draw from p_j
     }
     if (sm.bc[2] == c) {
-      // this tile holds the crossing: the first positive-mass element whose
-      // running total passes tau, and the last positive-mass element should
-      // rounding leave none, each thread walking its elements in order
+      // this tile holds the crossing.  Running totals only grow along a
+      // thread's elements, so the first element past tau lies in the first
+      // thread whose total passes it, and only that thread walks its elements
+      // (should rounding leave no element past tau: the tile's last
+      // positive-mass element, in the last thread with mass)
       const double prefix = sm.dbc[0], tau = sm.dbc[1];
-      float o1 = ot, o2 = od;
-      asm volatile("" : "+v"(o1), "+v"(o2));
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s) asm volatile("" : "+v"(rt[s]), "+v"(rd[s]));
-      int first = 0x7fffffff, lastpos = -1;
-      if (mine > 0.f) {
-        float a = 0.f;
-#pragma unroll
-        for (int s = 0; s < NSEG; ++s)
-#pragma unroll
-          for (int w = 0; w < W; ++w) {
-            const float m = draw_mass<DT>(rt[s], rd[s], w, rmode, o1, o2, P.sc);
-            a += m;
-            if (m > 0.f) {
-              if (first == 0x7fffffff && prefix + (base + (double)a) > tau) first = dpos<DT>(s, w);
-              lastpos = dpos<DT>(s, w);
-            }
-          }
-      }
-      first = wave_min_i(first);
-      lastpos = wave_max_i(lastpos);
-      if (lane == 0) { sm.i[2][wid] = first; sm.i[3][wid] = lastpos; }
+      const bool past = mine > 0.f && prefix + (base + (double)mine) > tau;
+      const int tfirst = wave_min_i(past ? tid : 0x7fffffff);
+      const int tlast = wave_max_i(mine > 0.f ? tid : -1);
+      if (lane == 0) { sm.i[2][wid] = tfirst; sm.i[3][wid] = tlast; }
       __syncthreads();
-      if (tid == 0) {
-        int f = sm.i[2][0], l = sm.i[3][0];
-        for (int w = 1; w < NWAVE; ++w) {
-          f = sm.i[2][w] < f ? sm.i[2][w] : f;
-          l = sm.i[3][w] > l ? sm.i[3][w] : l;
+      int tf = sm.i[2][0], tl = sm.i[3][0];
+      for (int w = 1; w < NWAVE; ++w) {
+        tf = sm.i[2][w] < tf ? sm.i[2][w] : tf;
+        tl = sm.i[3][w] > tl ? sm.i[3][w] : tl;
+      }
+      const int walker = tf != 0x7fffffff ? tf : tl;
+      if (walker >= 0 && wid == (walker >> 6)) {
+        float o1 = ot, o2 = od;
+        asm volatile("" : "+v"(o1), "+v"(o2));
+#pragma unroll
+        for (int s = 0; s < NSEG; ++s) asm volatile("" : "+v"(rt[s]), "+v"(rd[s]));
+        int first = 0x7fffffff, lastpos = -1;
+        if (tid == walker) {
+          float a = 0.f;
+#pragma unroll
+          for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+              const float m = draw_mass<DT>(rt[s], rd[s], w, rmode, o1, o2, P.sc);
+              a += m;
+              if (m > 0.f) {
+                if (first == 0x7fffffff && prefix + (base + (double)a) > tau) first = dpos<DT>(s, w);
+                lastpos = dpos<DT>(s, w);
+              }
+            }
+          const int pos = first != 0x7fffffff ? first : lastpos;
+          // the token stands unless the assembly found a data error
+          if (wait_at_least(&rec->state, 1, P.fault) == 1)
+            P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
         }
-        const int pos = f != 0x7fffffff ? f : l;
-        // the token stands unless the assembly found a data error
-        if (wait_at_least(&rec->state, 1, P.fault) == 1)
-          P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+      } else if (walker < 0 && tid == 0) {
+        if (wait_at_least(&rec->state, 1, P.fault) == 1) P.out_tokens[(int64_t)b * K1 + j] = -1;
       }
     }
   }
   // every draw workgroup of the sequence reports; the last clears its state
-  const int old = arrive(P.ddone + (int64_t)b * CTR, &sm.bc[7]);
+  const int old = count_done(P.ddone + (int64_t)b * CTR, &sm.bc[7]);
   if (old != nT - 1) {
     if ((old < 0 || old >= nT) && tid == 0) atomicOr(P.fault, 2);
     return;

@@ -168,10 +168,13 @@ __device__ __forceinline__ uint64_t tot_word(double t) {
 }
 __device__ __forceinline__ double tot_value(uint64_t w) { return __builtin_bit_cast(double, ~w); }
 
-// Announce this workgroup's published data on a counter; returns the count
-// before it (the same value in every thread), passed through the LDS word slot.
-__device__ __forceinline__ int arrive(int32_t *ctr, int32_t *slot) {
-  block_stores_done();
+// Count this workgroup as done with the shared state it read; returns the
+// count before it (the same value in every thread), passed through the LDS word
+// slot.  Its stores need not complete first: the last one to count only clears
+// state the others have read, and their reads are complete (their values were
+// used before the barrier).
+__device__ __forceinline__ int count_done(int32_t *ctr, int32_t *slot) {
+  __syncthreads();
   if (threadIdx.x == 0) *slot = add_dev(ctr, 1);
   __syncthreads();
   const int old = *slot;

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
 
   // ---- the row's last tile clears its words; the last row sums the loss
   if (c == 0 && wid == 0 && lane == 0) sm.slot = last_row ? 1 : 0;
-  const int old = arrive(P.rdone + (int64_t)n * CTR, &sm.i[0]);
+  const int old = count_done(P.rdone + (int64_t)n * CTR, &sm.i[0]);
   if (old == nT - 1) {
     for (int q = tid; q < 3 * nT; q += TPB) st_dev(part + q, (uint64_t)0);
     if (tid == 0) st_dev(P.rdone + (int64_t)n * CTR, 0);
