@@ -135,6 +135,9 @@ struct Smem {
       int32_t part[TPB];
       uint64_t list[TOPK];
     } fb;
+    struct {                           // draw: the crossing thread's elements
+      uint32_t t[NSEG * 4], d[NSEG * 4];
+    } walk;
   };
   uint32_t w8[LIST];                   // stream: each wave's two largest lane maxima
   float f[4][NWAVE];
@@ -664,13 +667,26 @@ __device__ __forceinline__ void wave_stats(const Elems<DT> &e, float mt, float s
 // Mass of element w of a vector: max(0, p - q) in residual mode, else p, with
 // p = exp2(x * sc - ot) and q = exp2(y * sc - od), where ot = m_t * sc +
 // log2(s_t) folds the row max and normaliser into one offset (od likewise).
+__device__ __forceinline__ float mass_of(float x, float y, bool rmode, float ot, float od, float sc) {
+  const float p = __builtin_amdgcn_exp2f(fmaf(x, sc, -ot));
+  if (!rmode) return p;
+  const float r = p - __builtin_amdgcn_exp2f(fmaf(y, sc, -od));
+  return r > 0.f ? r : 0.f;
+}
 template <int DT>
 __device__ __forceinline__ float draw_mass(const u32x4 &vt, const u32x4 &vd, int w, bool rmode, float ot, float od,
                                            float sc) {
-  const float p = __builtin_amdgcn_exp2f(fmaf(unpack<DT>(vt, w), sc, -ot));
-  if (!rmode) return p;
-  const float r = p - __builtin_amdgcn_exp2f(fmaf(unpack<DT>(vd, w), sc, -od));
-  return r > 0.f ? r : 0.f;
+  return mass_of(unpack<DT>(vt, w), unpack<DT>(vd, w), rmode, ot, od, sc);
+}
+
+// Element e of a thread's draw-order elements, held as 32-bit words.
+template <int DT> __device__ __forceinline__ float elem_of_words(const uint32_t *words, int e) {
+  if constexpr (DT == SV_BF16) {
+    const uint32_t word = words[e >> 1];
+    return __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+  } else {
+    return __uint_as_float(words[e]);
+  }
 }
 
 // Draw workgroup (b, c), dispatched after every streaming workgroup.  It
@@ -798,9 +814,11 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
     if (sm.bc[2] == c) {
       // this tile holds the crossing.  Running totals only grow along a
       // thread's elements, so the first element past tau lies in the first
-      // thread whose total passes it, and only that thread walks its elements
-      // (should rounding leave no element past tau: the tile's last
-      // positive-mass element, in the last thread with mass)
+      // thread whose total passes it (should rounding leave no element past
+      // tau: the tile's last positive-mass element, in the last thread with
+      // mass).  That thread hands its elements to wave 0, whose lanes compute
+      // one mass each and form the thread's running totals in its own order,
+      // so the last of them equals its total bit for bit.
       const double prefix = sm.dbc[0], tau = sm.dbc[1];
       const bool past = mine > 0.f && prefix + (base + (double)mine) > tau;
       const int tfirst = wave_min_i(past ? tid : 0x7fffffff);
@@ -813,32 +831,36 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
         tl = sm.i[3][w] > tl ? sm.i[3][w] : tl;
       }
       const int walker = tf != 0x7fffffff ? tf : tl;
-      if (walker >= 0 && wid == (walker >> 6)) {
-        float o1 = ot, o2 = od;
-        asm volatile("" : "+v"(o1), "+v"(o2));
+      if (tid == walker) {
 #pragma unroll
-        for (int s = 0; s < NSEG; ++s) asm volatile("" : "+v"(rt[s]), "+v"(rd[s]));
-        int first = 0x7fffffff, lastpos = -1;
-        if (tid == walker) {
-          float a = 0.f;
+        for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-          for (int s = 0; s < NSEG; ++s)
+          for (int q = 0; q < 4; ++q) { sm.walk.t[s * 4 + q] = rt[s][q]; sm.walk.d[s * 4 + q] = rd[s][q]; }
+        sm.dbc[3] = base;
+      }
+      __syncthreads();
+      if (wid == 0) {
+        constexpr int NE = NSEG * W;                     // elements per thread (<= 64)
+        int pos = -1;
+        if (walker >= 0) {
+          const float m = lane < NE ? mass_of(elem_of_words<DT>(sm.walk.t, lane), elem_of_words<DT>(sm.walk.d, lane),
+                                              rmode, ot, od, P.sc)
+                                    : 0.f;
+          float a = 0.f, al = 0.f;
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-              const float m = draw_mass<DT>(rt[s], rd[s], w, rmode, o1, o2, P.sc);
-              a += m;
-              if (m > 0.f) {
-                if (first == 0x7fffffff && prefix + (base + (double)a) > tau) first = dpos<DT>(s, w);
-                lastpos = dpos<DT>(s, w);
-              }
-            }
-          const int pos = first != 0x7fffffff ? first : lastpos;
-          // the token stands unless the assembly found a data error
-          if (wait_at_least(&rec->state, 1, P.fault) == 1)
-            P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+          for (int l = 0; l < NE; ++l) {
+            a += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), l));
+            al = lane == l ? a : al;
+          }
+          const double wbase = sm.dbc[3];
+          const uint64_t pass = __ballot(m > 0.f && prefix + (wbase + (double)al) > tau);
+          const uint64_t posm = __ballot(m > 0.f);
+          const int e = pass ? __builtin_ctzll(pass) : (posm ? 63 - __builtin_clzll(posm) : -1);
+          pos = e < 0 ? -1 : walker * NE + e;
         }
-      } else if (walker < 0 && tid == 0) {
-        if (wait_at_least(&rec->state, 1, P.fault) == 1) P.out_tokens[(int64_t)b * K1 + j] = -1;
+        // the token stands unless the assembly found a data error
+        if (lane == 0 && wait_at_least(&rec->state, 1, P.fault) == 1)
+          P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
       }
     }
   }
