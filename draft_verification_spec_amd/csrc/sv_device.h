@@ -235,11 +235,12 @@ template <int DT> __device__ __forceinline__ int dpos(int s, int w) {
 
 // Load one tile of a row into registers; entries past V read as -inf.
 // Streaming (TM false): vector s of a thread sits at tpos (vectors interleaved
-// over the threads) and the loads are marked nontemporal, since each logit is
-// read once.  Draw (TM true): vector s sits at dpos (each thread's vectors
-// consecutive) with ordinary loads, which measured faster for this re-read.
-// NS vectors per thread (a tile of TPB * NS * W entries; NSEG unless given).
-template <int DT, bool TM = false, int NS = NSEG>
+// over the threads).  Draw (TM true): vector s sits at dpos (each thread's
+// vectors consecutive).  NT marks the loads nontemporal (the default for
+// streaming, where each logit is read once; the draw's re-read measured
+// faster with ordinary loads).  NS vectors per thread (a tile of TPB * NS * W
+// entries; NSEG unless given).
+template <int DT, bool TM = false, int NS = NSEG, bool NT = !TM>
 __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool vec, u32x4 (&r)[NS]) {
   static_assert(!TM || NS == NSEG, "the draw order is defined for NSEG vectors");
   constexpr int E = Fmt<DT>::E, W = Fmt<DT>::W;
@@ -248,8 +249,8 @@ __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool ve
   for (int s = 0; s < NS; ++s) {
     const int64_t e0 = c0 + (TM ? dpos<DT>(s, 0) : tpos<DT>(s, 0));
     if (vec && e0 + W <= V) {
-      if (TM) r[s] = *(const u32x4 *)(row + e0 * E);
-      else r[s] = __builtin_nontemporal_load((const u32x4 *)(row + e0 * E));
+      if (NT) r[s] = __builtin_nontemporal_load((const u32x4 *)(row + e0 * E));
+      else r[s] = *(const u32x4 *)(row + e0 * E);
     } else {
       u32x4 v;
 #pragma unroll
