@@ -17,8 +17,10 @@
 // workgroup of the row polls all of them (lane = tile) and combines them in
 // tile order into the row's log-normaliser, the same bits in each workgroup.
 // The row's workgroups are consecutive and wait (bounded) only for one
-// another.  Tile 0 computes the KL and the row's loss term; the workgroup that
-// publishes the last term sums all of them in row order.
+// another.  Tile 0 computes the KL and the row's loss term, and clears the
+// row's words once every tile has read them; the workgroup that publishes the
+// last term sums all of them in row order.  A stored id's gradient entry is
+// patched by the thread that wrote the entry's vector, after it.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -72,6 +74,9 @@ struct KSmem {
   double pt[KTOP];                       // softmax of the stored entries (wave 1)
   double lpt[KTOP];                      // its logarithm
   int32_t px[KTOP];                      // token id of a used entry, else -1
+  int32_t pcnt;                          // used entries whose id falls in this tile (wave 1)
+  int32_t ppos[KTOP];                    // their positions in the tile, in entry order
+  double ppt[KTOP];                      // and their pt
   double red[NWAVE];                     // final loss reduction
   int32_t slot;                          // counter values
 };
@@ -144,6 +149,7 @@ __device__ __forceinline__ void store_grad(char *grow, int64_t col0, int V, bool
   }
 }
 
+// w * q over one tile: the thread's vectors, as stored at tpos.
 template <int DT, int GT>
 __device__ __forceinline__ void grad_tile(const KParams &P, const u32x4 (&r)[KSEG], int n, int c, bool zero,
                                           float hi, float corr, float wf) {
@@ -233,6 +239,8 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
       if (a1 == 0) a1 = ld_dev(part + 3 * lane + 1);
       if (a2 == 0) a2 = ld_dev(part + 3 * lane + 2);
     }
+    // this workgroup has read the row's words (their values are in hand)
+    if (lane == 0) add_dev_noret(P.rdone + (int64_t)n * CTR, 1);
     const float mc = lane < nT ? (float)tot_value(a0) : NEG_INF;
     const float M = wave_max_f(mc);
     const double S = wave_sum_d(lane < nT ? rescale(tot_value(a1), mc, M, sc) : 0.0);
@@ -266,7 +274,15 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
       sm.lpt[lane] = use ? a - log(Sv) : 0.0;
       sm.px[lane] = use ? x : -1;
     }
-    if (lane == 0) { sm.w = w; sm.eflags = F; }
+    // the entries whose id falls in this tile, in entry order
+    const bool here = use && x >= c * TILE && x < c * TILE + TILE;
+    const uint64_t hm = __ballot(here);
+    if (here) {
+      const int q = __popcll(hm & ((1ull << lane) - 1));
+      sm.ppos[q] = x - c * TILE;
+      sm.ppt[q] = e / Sv;
+    }
+    if (lane == 0) { sm.w = w; sm.eflags = F; sm.pcnt = __popcll(hm); }
   }
   __syncthreads();
   const int F = sm.zflags | sm.eflags;
@@ -296,7 +312,10 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
   }
 
   // ---- the gradient of this tile: w * q everywhere, then w * (q - pt) at the
-  // stored ids that fall in it
+  // stored ids that fall in it.  A patch is written by the thread that wrote
+  // the entry's vector, after it in program order, so it lands last without a
+  // wait for the tile's stores; entries go in entry order, so a repeated id
+  // keeps its last one.
   if (P.grad) {
     const float hi = (float)lse2, lo = (float)(lse2 - (double)hi);
     const float corr = 1.f - lo * (float)LN2;
@@ -305,13 +324,14 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
     for (int s = 0; s < KSEG; ++s) asm volatile("" : "+v"(r[s]));
     if (P.gdt == SV_BF16) grad_tile<DT, SV_BF16>(P, r, n, c, F != 0, hi, corr, wf);
     else grad_tile<DT, SV_F32>(P, r, n, c, F != 0, hi, corr, wf);
-    block_stores_done();
-    if (wid == 0 && !F) {
-      const int x = lane < KTOP ? sm.px[lane] : -1;
-      if (x >= c * TILE && x < c * TILE + TILE) {
+    const int npatch = F ? 0 : sm.pcnt;
+    for (int e = 0; e < npatch; ++e) {
+      const int p = sm.ppos[e];
+      if ((p / W) % TPB == tid) {
+        const int64_t x = (int64_t)c * TILE + p;
         const float zx = load_elem<DT>(row, x);
         const float q = __builtin_amdgcn_exp2f(fmaf(zx, sc, -hi)) * corr;
-        const float g = (float)((double)wf * ((double)q - sm.pt[lane]));
+        const float g = (float)((double)wf * ((double)q - sm.ppt[e]));
         char *grow = P.grad + (int64_t)n * P.V * (P.gdt == SV_BF16 ? 2 : 4);
         if (P.gdt == SV_BF16) ((uint16_t *)grow)[x] = (uint16_t)grad_bits<SV_BF16>(g);
         else ((float *)grow)[x] = g;
@@ -319,16 +339,19 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
     }
   }
 
-  // ---- the row's last tile clears its words; the last row sums the loss
-  if (c == 0 && wid == 0 && lane == 0) sm.slot = last_row ? 1 : 0;
-  const int old = count_done(P.rdone + (int64_t)n * CTR, &sm.i[0]);
-  if (old == nT - 1) {
-    for (int q = tid; q < 3 * nT; q += TPB) st_dev(part + q, (uint64_t)0);
-    if (tid == 0) st_dev(P.rdone + (int64_t)n * CTR, 0);
-  } else if (old < 0 || old >= nT) {
-    if (tid == 0) atomicOr(P.fault, 2);
+  // ---- tile 0 clears the row's words once every tile has read them (the
+  // others report right after reading, long before tile 0 gets here); the
+  // last row sums the loss
+  if (c != 0) return;
+  if (tid == 0) {
+    sm.slot = last_row ? 1 : 0;
+    const int v = wait_at_least(P.rdone + (int64_t)n * CTR, nT, P.fault);
+    if (v > nT) atomicOr(P.fault, 2);                  // workspace not zero-filled
   }
-  if (c != 0 || !sm.slot) return;
+  __syncthreads();
+  for (int q = tid; q < 3 * nT; q += TPB) st_dev(part + q, (uint64_t)0);
+  if (tid == 0) st_dev(P.rdone + (int64_t)n * CTR, 0);
+  if (!sm.slot) return;
   // every row's term is published: sum them in row order (a fixed chunk per
   // thread, then the waves in order), then clear them
   const int N = P.N, ch = (N + TPB - 1) / TPB;
