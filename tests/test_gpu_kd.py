@@ -122,6 +122,25 @@ def test_error_rows_and_clip(sv, oracle_mod):
     assert loss_ok(g, o)
 
 
+def test_repeated_stored_ids(sv, oracle_mod):
+    """A stored id listed more than once: the KL counts every entry, and the
+    gradient entry keeps the last one's w * (q - pt), as in the oracle (which
+    writes the entries in order)."""
+    w = sv_inputs.kd_workload("kd_dup", 8, 4, 2, 20000, sv_inputs.BF16, 1500)
+    w.topk_idx[0, 7] = w.topk_idx[0, 2]           # twice, entries far apart in value
+    w.topk_idx[3, 30] = w.topk_idx[3, 31]         # the two smallest entries
+    w.topk_idx[5, [4, 9, 20]] = w.topk_idx[5, 1]  # four times
+    w.topk_val[5, 20] = w.topk_val[5, 0]          # one of them with the row's largest value
+    o = oracle_mod.kd_workload(w)
+    assert (o.status == 0).all()
+    g = run_kd(sv, w, "f32")
+    check(w, o, g, grad_dtype="f32")
+    assert loss_ok(g, o)
+    for n, j in ((0, 7), (3, 31), (5, 20)):      # the last entry of each repeated id
+        x = w.topk_idx[n, j]
+        np.testing.assert_allclose(g["grad"][n, x], o.grad[n, x], rtol=1e-5, atol=1e-9)
+
+
 def test_full_vocabulary_rows(sv, oracle_mod):
     """V = 151936 bf16 rows (19 tiles) in the rollout workload's layout."""
     w = sv_inputs.kd_workload("kd_full", 16, 8, 4, 151936, sv_inputs.BF16, 1400)
