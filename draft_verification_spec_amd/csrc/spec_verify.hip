@@ -642,7 +642,7 @@ template <int DT> __device__ __forceinline__ void unpack_all(const u32x4 (&r)[NS
 template <int DT> __device__ __forceinline__ float vmax_of(const Elems<DT> &e, int s) {
   float m = e.x[s][0];
 #pragma unroll
-  for (int w = 1; w < Fmt<DT>::W; ++w) m = fmaxf(m, e.x[s][w]);
+  for (int w = 1; w < Fmt<DT>::W; ++w) m = fmax_nan(m, e.x[s][w]);
   return m;
 }
 template <int DT> __device__ __forceinline__ bool has_nan_of(const Elems<DT> &e) {
@@ -922,7 +922,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
     unpack_all<DT>(rd, ed);
     float md = vmax_of<DT>(ed, 0);
 #pragma unroll
-    for (int s = 1; s < NSEG; ++s) md = fmaxf(md, vmax_of<DT>(ed, s));
+    for (int s = 1; s < NSEG; ++s) md = fmax_nan(md, vmax_of<DT>(ed, s));
     wave_stats<DT>(ed, md, P.sc, wm_d, ws_d, wf_d);
   }
   Elems<DT> et;
@@ -932,12 +932,12 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
   for (int s = 0; s < NSEG; ++s) vmt[s] = vmax_of<DT>(et, s);
   float mt = vmt[0];
 #pragma unroll
-  for (int s = 1; s < NSEG; ++s) mt = fmaxf(mt, vmt[s]);
+  for (int s = 1; s < NSEG; ++s) mt = fmax_nan(mt, vmt[s]);
   if (!GREEDY) {
     wave_stats<DT>(et, mt, P.sc, wm_t, ws_t, wf_t);
   } else {
     wm_t = wave_max_f(mt);
-    wf_t = __ballot(has_nan_of<DT>(et)) ? SV_STATUS_NAN : 0;   // the maxima skip NaN: test every element
+    wf_t = __ballot(has_nan_of<DT>(et)) ? SV_STATUS_NAN : 0;   // no exp sums here: test every element
   }
 
   // the wave's two largest lane maxima
