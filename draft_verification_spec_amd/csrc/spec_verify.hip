@@ -32,10 +32,12 @@
 //  draw       The draw workgroups of a sequence learn the drawing row from the
 //             group records as soon as it is decided: pair row j after a
 //             rejection (residual max(0, p - q)), row k after k acceptances
-//             (p).  Each publishes one tile's total mass; once all tiles of
-//             the row are in, every one finds the crossing tile of u * R over
-//             the totals in tile order, and the one that holds it draws the
-//             token from its registers.
+//             (p).  For a residual each publishes one tile's total mass; once
+//             all tiles of the row are in, every one finds the crossing tile of
+//             u * R over the totals in tile order, and the one that holds it
+//             draws the token from its registers.  For the bonus row the tile
+//             masses follow from the row's streaming statistics, so only the
+//             workgroup of the crossing tile reads its elements.
 //
 // A streaming workgroup only ever waits for workgroups of lower items, which
 // its XCD dispatches first (items run in order within an XCD; a group or a
@@ -614,8 +616,12 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     if (a < nslot && key[q]) st_dev(slots + a, (uint64_t)0);
   }
   if (own) {
+    // (sampling: row k's maximum and sum words stay for a bonus draw; the
+    // sequence's last draw workgroup clears them)
+    const int q0 = !GREEDY && i == k ? 2 : 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) st_dev(rsrc + q, (uint64_t)0);
+    for (int q = 0; q < 8; ++q)
+      if (q >= q0) st_dev(rsrc + q, (uint64_t)0);
   }
   if (ov) st_dev(P.ovf + (int64_t)g * nT + lane, 0);
   if (!GREEDY || i != k) return;
@@ -699,20 +705,87 @@ template <int DT> __device__ __forceinline__ float elem_of_words(const uint32_t 
   }
 }
 
+// The draw in the workgroup whose tile holds the crossing: thread t's own
+// mass `mine` and the mass `base` of the tile's elements before it, the tile's
+// elements rt (and rd for a residual) in registers, the mass before the tile
+// and tau in sm.dbc[0..1].
+template <int DT>
+__device__ __forceinline__ void draw_crossing(const Params &P, int b, int c, int j, const u32x4 (&rt)[NSEG],
+                                              const u32x4 (&rd)[NSEG], bool rmode, float ot, float od, float mine,
+                                              double base, SeqRec *rec, Smem &sm) {
+  constexpr int W = Fmt<DT>::W;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K1 = P.k + 1;
+  // this tile holds the crossing.  Running totals only grow along a
+  // thread's elements, so the first element past tau lies in the first
+  // thread whose total passes it (should rounding leave no element past
+  // tau: the tile's last positive-mass element, in the last thread with
+  // mass).  That thread hands its elements to wave 0, whose lanes compute
+  // one mass each and form the thread's running totals in its own order,
+  // so the last of them equals its total bit for bit.
+  const double prefix = sm.dbc[0], tau = sm.dbc[1];
+  const bool past = mine > 0.f && prefix + (base + (double)mine) > tau;
+  const int tfirst = wave_min_i(past ? tid : 0x7fffffff);
+  const int tlast = wave_max_i(mine > 0.f ? tid : -1);
+  if (lane == 0) { sm.i[2][wid] = tfirst; sm.i[3][wid] = tlast; }
+  __syncthreads();
+  int tf = sm.i[2][0], tl = sm.i[3][0];
+  for (int w = 1; w < NWAVE; ++w) {
+    tf = sm.i[2][w] < tf ? sm.i[2][w] : tf;
+    tl = sm.i[3][w] > tl ? sm.i[3][w] : tl;
+  }
+  const int walker = tf != 0x7fffffff ? tf : tl;
+  if (tid == walker) {
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { sm.walk.t[s * 4 + q] = rt[s][q]; sm.walk.d[s * 4 + q] = rd[s][q]; }
+    sm.dbc[3] = base;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    constexpr int NE = NSEG * W;                     // elements per thread (<= 64)
+    int pos = -1;
+    if (walker >= 0) {
+      const float m = lane < NE ? mass_of(elem_of_words<DT>(sm.walk.t, lane), elem_of_words<DT>(sm.walk.d, lane),
+                                          rmode, ot, od, P.sc)
+                                : 0.f;
+      float a = 0.f, al = 0.f;
+#pragma unroll
+      for (int l = 0; l < NE; ++l) {
+        a += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), l));
+        al = lane == l ? a : al;
+      }
+      const double wbase = sm.dbc[3];
+      const uint64_t pass = __ballot(m > 0.f && prefix + (wbase + (double)al) > tau);
+      const uint64_t posm = __ballot(m > 0.f);
+      const int e = pass ? __builtin_ctzll(pass) : (posm ? 63 - __builtin_clzll(posm) : -1);
+      pos = e < 0 ? -1 : walker * NE + e;
+    }
+    // the token stands unless the assembly found a data error
+    if (lane == 0 && wait_at_least(&rec->state, 1, P.fault) == 1)
+      P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+  }
+}
+
 // Draw workgroup (b, c), dispatched after every streaming workgroup.  It
 // learns the drawing row j of sequence b from the group records as soon as it
 // is decided: the first rejected draft (all earlier ones accepted), or row k
 // once all k drafts are accepted; with more than 63 drafts it waits for the
-// sequence's assembly instead.  It publishes tile c's total mass of the drawing
-// row (the residual max(0, p_j - q_j) for j < k, p_k for j == k), waits for
-// the row's other tiles, finds the crossing tile of tau = u * R over the totals
-// in tile order, and if it holds that tile draws the first positive-mass
-// element whose cumulative mass exceeds tau (the tile's last positive-mass
-// element should rounding leave none), written once the assembly has found no
-// data error.  A residual with no mass left (only through rounding) is
-// replaced by p_j in a second round.  Cumulative masses are the fixed-order
-// fp64 scan of fp32 per-thread sums, the same arithmetic for the totals and
-// for the draw.  A sequence's draw workgroups are consecutive, so each waits
+// sequence's assembly instead.  For a residual (j < k) it publishes tile c's
+// total mass of max(0, p_j - q_j), waits for the row's other tiles and finds
+// the crossing tile of tau = u * R over the totals in tile order; for the
+// bonus (j == k) the tile masses of p_k come from row k's tile records
+// (sum times 2^(max * sc - ot)), so no tile is read before the crossing is
+// known.  The workgroup that holds the crossing tile draws the first
+// positive-mass element whose cumulative mass exceeds tau (the tile's last
+// positive-mass element should rounding leave none), written once the
+// assembly has found no data error.  A residual with no mass left (only through rounding) is
+// replaced by p_j in a second round.  Within a tile, cumulative masses are the
+// fixed-order fp64 scan of fp32 per-thread sums (for a residual the same
+// arithmetic as its tile totals; a bonus tile's total from the statistics
+// agrees with its elements' sum to rounding, and the fallback above covers a
+// crossing that rounding moves past the tile's end).  A sequence's draw workgroups are consecutive, so each waits
 // only for workgroups dispatched with it or before it.  The last one to finish
 // clears the sequence's state.
 template <int DT>
@@ -763,8 +836,43 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
   __syncthreads();
   const int j = sm.bc[3];
   uint64_t *tot = P.dtot + (int64_t)b * nT * 2;
-  if (j >= 0) {
-    const bool resid = j < k;
+  if (j == k) {
+    // bonus draw: the crossing tile straight from row k's streaming
+    // statistics, which its merge leaves for the draw.  Tile t's mass under
+    // p = exp2(x * sc - ot) is s_t * 2^(m_t * sc - ot), s_t its sum of
+    // exp2((x - m_t) * sc) (lane t, in tile order); only the workgroup that
+    // holds the crossing reads its elements
+    const float ot = sm.f[2][0];
+    if (wid == 0) {
+      const uint64_t *rk = (const uint64_t *)(P.recs + (int64_t)(b * K1 + k) * nT) + lane * 8;
+      const bool own = lane < nT;
+      const uint64_t w0 = own ? ld_dev(rk) : 0ull, w1 = own ? ld_dev(rk + 1) : 0ull;
+      const float mt = __uint_as_float((uint32_t)w0);
+      const double tm = own && mt != NEG_INF
+                            ? __builtin_bit_cast(double, w1) * exp2_split((double)mt * (double)P.sc - (double)ot)
+                            : 0.0;
+      const double cum = wave_scan_d(tm);
+      const double tau = sm.dbc[2] * readlane_d(cum, 63);
+      const uint64_t h = __ballot(own && cum > tau);
+      const int cs = h ? __builtin_ctzll(h) : nT - 1;
+      const double before = cs > 0 ? readlane_d(cum, cs - 1) : 0.0;
+      if (lane == 0) { sm.bc[2] = cs; sm.dbc[0] = before; sm.dbc[1] = tau; }
+    }
+    __syncthreads();
+    if (sm.bc[2] == c) {
+      u32x4 rt[NSEG];
+      load_tile<DT, true>(P.target + ((int64_t)b * K1 + k) * P.tstride * Fmt<DT>::E, c, P.V, P.t_vec, rt);
+      float a = 0.f;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+        for (int w = 0; w < W; ++w) a += draw_mass<DT>(rt[s], rt[s], w, false, ot, 0.f, P.sc);
+      double base;
+      block_scan_d((double)a, base, sm.d[0]);
+      draw_crossing<DT>(P, b, c, j, rt, rt, false, ot, 0.f, a, base, rec, sm);
+    }
+  } else if (j >= 0) {
+    const bool resid = true;           // j < k: the residual of pair row j
     const float ot = sm.f[2][0], od = sm.f[2][1];
     const double u = sm.dbc[2];
     const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
@@ -821,58 +929,7 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
       if (!sm.bc[4]) break;
       rmode = false;                   // no residual mass left: draw from p_j
     }
-    if (sm.bc[2] == c) {
-      // this tile holds the crossing.  Running totals only grow along a
-      // thread's elements, so the first element past tau lies in the first
-      // thread whose total passes it (should rounding leave no element past
-      // tau: the tile's last positive-mass element, in the last thread with
-      // mass).  That thread hands its elements to wave 0, whose lanes compute
-      // one mass each and form the thread's running totals in its own order,
-      // so the last of them equals its total bit for bit.
-      const double prefix = sm.dbc[0], tau = sm.dbc[1];
-      const bool past = mine > 0.f && prefix + (base + (double)mine) > tau;
-      const int tfirst = wave_min_i(past ? tid : 0x7fffffff);
-      const int tlast = wave_max_i(mine > 0.f ? tid : -1);
-      if (lane == 0) { sm.i[2][wid] = tfirst; sm.i[3][wid] = tlast; }
-      __syncthreads();
-      int tf = sm.i[2][0], tl = sm.i[3][0];
-      for (int w = 1; w < NWAVE; ++w) {
-        tf = sm.i[2][w] < tf ? sm.i[2][w] : tf;
-        tl = sm.i[3][w] > tl ? sm.i[3][w] : tl;
-      }
-      const int walker = tf != 0x7fffffff ? tf : tl;
-      if (tid == walker) {
-#pragma unroll
-        for (int s = 0; s < NSEG; ++s)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { sm.walk.t[s * 4 + q] = rt[s][q]; sm.walk.d[s * 4 + q] = rd[s][q]; }
-        sm.dbc[3] = base;
-      }
-      __syncthreads();
-      if (wid == 0) {
-        constexpr int NE = NSEG * W;                     // elements per thread (<= 64)
-        int pos = -1;
-        if (walker >= 0) {
-          const float m = lane < NE ? mass_of(elem_of_words<DT>(sm.walk.t, lane), elem_of_words<DT>(sm.walk.d, lane),
-                                              rmode, ot, od, P.sc)
-                                    : 0.f;
-          float a = 0.f, al = 0.f;
-#pragma unroll
-          for (int l = 0; l < NE; ++l) {
-            a += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), l));
-            al = lane == l ? a : al;
-          }
-          const double wbase = sm.dbc[3];
-          const uint64_t pass = __ballot(m > 0.f && prefix + (wbase + (double)al) > tau);
-          const uint64_t posm = __ballot(m > 0.f);
-          const int e = pass ? __builtin_ctzll(pass) : (posm ? 63 - __builtin_clzll(posm) : -1);
-          pos = e < 0 ? -1 : walker * NE + e;
-        }
-        // the token stands unless the assembly found a data error
-        if (lane == 0 && wait_at_least(&rec->state, 1, P.fault) == 1)
-          P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
-      }
-    }
+    if (sm.bc[2] == c) draw_crossing<DT>(P, b, c, j, rt, rd, rmode, ot, od, mine, base, rec, sm);
   }
   // every draw workgroup of the sequence reports; the last clears its state
   const int old = count_done(P.ddone + (int64_t)b * CTR, &sm.bc[7]);
@@ -886,6 +943,10 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
   for (int q = tid; q < 2 * nT; q += TPB) st_dev(tot + q, (uint64_t)0);
   zero_recs(rec, 1);
   zero_recs(P.grec + (int64_t)b * K1, K1);
+  {
+    uint64_t *rk = (uint64_t *)(P.recs + (int64_t)(b * K1 + k) * nT);   // row k's words 0-1, left by its merge
+    for (int q = tid; q < 2 * nT; q += TPB) st_dev(rk + (q >> 1) * 8 + (q & 1), (uint64_t)0);
+  }
   if (tid == 0) st_dev(P.ddone + (int64_t)b * CTR, 0);
 }
 
