@@ -7,8 +7,9 @@ uses (csrc/sv_dispatch.h) with a summary (profiles/dispatch_layout_V151936.md).
 Inputs are timing inputs only, generated on the device (seeded): target logits
 N(0, 3^2), draft = target + N(0, 1), drafted tokens drawn from the draft
 softmax by the Gumbel-max trick, uniforms U[0, 1).  Each configuration runs
-both layouts back to back (several input copies rotate, up to 1 GB), twice in
-alternation; the table keeps the faster layout.  The layouts give identical
+both layouts back to back (several input copies rotate, up to 1 GB), 60 steps
+each, five times in alternation; the table keeps the layout with the lower
+best time.  The layouts give identical
 results; only the order in which streaming workgroups take the (group, tile)
 items differs.
 """
@@ -36,14 +37,14 @@ def make_inputs(torch, dt, greedy, B, k, seed):
     return t.to(tt), d.to(tt), x, u
 
 
-def measure(torch, sv, dt, greedy, B, k, steps=20):
+def measure(torch, sv, dt, greedy, B, k, steps=60, rounds=5):
     t, d, x, u = make_inputs(torch, dt, greedy, B, k, 7000 + B * 31 + k)
     size = t.numel() * t.element_size() + (0 if greedy else d.numel() * d.element_size())
     copies = max(1, min(64, -(-(1 << 30) // size)))
     sets = [(t, d)] + [(t.clone(), d.clone()) for _ in range(copies - 1)]
     T = 0.0 if greedy else 1.0
     best = {}
-    for rnd in range(2):
+    for rnd in range(rounds):
         for layout in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS):
             def step(i):
                 a, b = sets[i % copies]
