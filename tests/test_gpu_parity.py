@@ -192,6 +192,26 @@ def test_k_zero(sv, orc, T):
     check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
 
 
+@pytest.mark.parametrize("dtype", [sv_inputs.BF16, sv_inputs.F32])
+def test_bonus_draw_tile_edges(sv, orc, dtype):
+    """Bonus draws (every draft accepted: draft rows equal the target rows)
+    whose row k has whole tiles of -inf, mass only in a middle tile, only in
+    the ragged last tile, or spread over every tile: the crossing tile comes
+    from the streaming statistics, the token from that tile's elements."""
+    V, k = 3 * 8192 + 1000, 2
+    w = sv_inputs.make_workload("bonus", 4, k, V, dtype, 1.0, 1951, 3.0, 0.5)
+    f = (lambda x: x) if dtype == sv_inputs.F32 else sv_inputs.bf16_round
+    tk = (w.target.astype(np.float32) if dtype == sv_inputs.F32 else sv_inputs.bf16_to_f32(w.target)).copy()
+    tk[0, k, :16384] = -np.inf                    # tiles 0-1 empty, mass in tiles 2-3
+    tk[1, k, :3 * 8192] = -np.inf                 # mass only in the ragged last tile
+    tk[2, k, 8192:16384] += 6.0                   # most mass in tile 1
+    w.target = f(tk)
+    w.draft = w.target[:, :k].copy()              # p = q: every draft accepted
+    o, g = orc.verify_workload(w), run_gpu(sv, w)
+    assert (o["accepted_len"] == k).all()
+    check_parity(o, g, w, exceptions_budget=False)
+
+
 @pytest.mark.parametrize("which", ["steady", "greedy"])
 def test_layouts_give_identical_results(sv, which):
     """The two item layouts only reorder which workgroup takes which item."""
