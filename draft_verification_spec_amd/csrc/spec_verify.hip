@@ -81,11 +81,11 @@ constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 // B = 1..256, k = 3..8), with fp32 logits nontemporal ones (7 us per step at
 // B = 32, k = 15).
 template <int DT> constexpr bool kStreamNT = DT == SV_F32;
-// Waves per SIMD the kernel is built for: the format's budget, but 8 for fp32
-// greedy (no exps or draws: 64 VGPRs, a spill of 8 bytes only on the merge's
-// rare rescan path; 83.6 -> 80.3 us at B = 32, k = 15).  bf16 greedy at 8
-// waves spills 112 bytes.
-template <int DT, bool GREEDY> constexpr int kWaves = (GREEDY && DT == SV_F32) ? 8 : Fmt<DT>::WAVES;
+// Waves per SIMD the kernel is built for: 8 for fp32 (64 VGPRs, a spill of 8
+// bytes only on the merge's rare rescan path; at B = 32, k = 15 greedy 83.6 ->
+// 80.3 us, sampling 135.6 -> 132.6 us); the format's budget for bf16, which
+// at 7 or 8 waves spills on hot paths (greedy at 8: 112 bytes).
+template <int DT, bool GREEDY> constexpr int kWaves = DT == SV_F32 ? 8 : Fmt<DT>::WAVES;
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
 // Published per (group, tile) by the stream workgroups; 8 words.
 struct TileRec {
