@@ -141,6 +141,7 @@ int spec_verify_layout_choice(const sv_shape_t *shape);
  *   row, bad uniform) cannot be seen without a device sync; they set the
  *   SV_STATUS_* bits of that sequence and make its accepted_len and
  *   out_tokens -1.
+ * B = 0: returns SV_OK after the argument checks and enqueues nothing.
  * Execution: one kernel launch.  Its streaming workgroups read every logit
  *   once (per-tile statistics and candidates, per-group merges, per-sequence
  *   assembly); in sampling mode draw workgroups follow (residual or bonus

@@ -86,6 +86,8 @@ size_t sv_kd_workspace_bytes(const sv_kd_shape_t *shape);
  * Errors: argument errors return a negative SV_ERR_* code before anything is
  *   enqueued.  Data errors set the row's status bits (a row_sample outside
  *   [0, S) counts as SV_KD_BAD_INDEX).
+ * N = 0: returns SV_OK, enqueues nothing and leaves every output, loss
+ *   included, untouched (the caller sets loss = 0 for an empty batch).
  * Execution: one kernel launch, one workgroup per (row, 16 KB tile).  The
  *   workgroups of a row exchange their tile statistics and wait (bounded) for
  *   one another; they are dispatched together.
