@@ -63,6 +63,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "spec_verify.h"
 #include "sv_device.h"
 #include "sv_dispatch.h"
@@ -1019,40 +1021,33 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
   for (int q = 0; q < LIST; ++q) { const uint32_t v = sm.w8[q]; if (v && v < kthr) kthr = v; }
   if (kthr == 0xffffffffu) kthr = 0u;
 
-  // candidates: elements at or above the threshold, to this tile's slots
+  // candidates: elements at or above the threshold, to this tile's slots,
+  // position by position (a position that holds none in any lane costs one
+  // compare; the slot reservation is one LDS atomic per wave and position)
   {
     const float thr = key_value(kthr);
     const int lim = V - c * TILE;                        // tile positions < lim exist
-    uint32_t mask = 0;
-    if (has_elem && tkey >= kthr) {
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s)
-        if (vmt[s] >= thr) {
-#pragma unroll
-          for (int w = 0; w < W; ++w)
-            if (tpos<DT>(s, w) < lim && et.x[s][w] >= thr) mask |= 1u << (s * W + w);
-        }
-    }
-    const int cnt = __popc(mask);
-    if (cnt) {
-      const int base = atomicAdd(&sm.bc[0], cnt);
-      uint64_t *dst = P.cand + (int64_t)item * SLOTS;
-      int slot = base;
+    const bool act = has_elem && tkey >= kthr;           // lanes that may hold candidates
+    uint64_t *dst = P.cand + (int64_t)item * SLOTS;
+    bool over = false;
+    auto walk = [&](auto full) {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) {
-        uint32_t m = (mask >> (s * W)) & ((1u << W) - 1u);
-        while (m) {
-          const int w = __builtin_ctz(m);
-          m &= m - 1;
-          float xv = et.x[s][0];                         // element w, by selection (no indexed registers)
+        if (act && vmt[s] >= thr) {
 #pragma unroll
-          for (int q = 1; q < W; ++q) xv = w == q ? et.x[s][q] : xv;
-          if (slot < SLOTS) st_dev(dst + slot, cand_key(xv, c * TILE + tpos<DT>(s, w)));
-          ++slot;
+          for (int w = 0; w < W; ++w) {
+            if ((decltype(full)::value || tpos<DT>(s, w) < lim) && et.x[s][w] >= thr) {
+              const int slot = atomicAdd(&sm.bc[0], 1);
+              if (slot < SLOTS) st_dev(dst + slot, cand_key(et.x[s][w], c * TILE + tpos<DT>(s, w)));
+              else over = true;
+            }
+          }
         }
       }
-      if (base + cnt > SLOTS) st_dev(P.ovf + item, 1);
-    }
+    };
+    if (lim >= TILE) walk(std::true_type());
+    else walk(std::false_type());
+    if (over) st_dev(P.ovf + item, 1);
   }
 
   // the tile record (wave 0: lanes 0-7 write one word each)
