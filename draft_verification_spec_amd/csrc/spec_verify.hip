@@ -143,7 +143,7 @@ struct Params {
 
 struct Smem {
   union {
-    uint64_t keys[MERGE_CAP];          // row merge: candidates at or above the bound
+    uint64_t keys[MERGE_CAP];          // stream: the tile's candidates; row merge: those at or above the bound
     struct {                           // exact top-32 fallback
       uint32_t hist[2048];
       int32_t part[TPB];
@@ -1021,15 +1021,13 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
   for (int q = 0; q < LIST; ++q) { const uint32_t v = sm.w8[q]; if (v && v < kthr) kthr = v; }
   if (kthr == 0xffffffffu) kthr = 0u;
 
-  // candidates: elements at or above the threshold, to this tile's slots,
-  // position by position (a position that holds none in any lane costs one
-  // compare; the slot reservation is one LDS atomic per wave and position)
+  // candidates: elements at or above the threshold, gathered in LDS position
+  // by position (a position that holds none in any lane costs one compare;
+  // the slot reservation is one LDS atomic per wave and position)
   {
     const float thr = key_value(kthr);
     const int lim = V - c * TILE;                        // tile positions < lim exist
     const bool act = has_elem && tkey >= kthr;           // lanes that may hold candidates
-    uint64_t *dst = P.cand + (int64_t)item * SLOTS;
-    bool over = false;
     auto walk = [&](auto full) {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) {
@@ -1038,8 +1036,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
           for (int w = 0; w < W; ++w) {
             if ((decltype(full)::value || tpos<DT>(s, w) < lim) && et.x[s][w] >= thr) {
               const int slot = atomicAdd(&sm.bc[0], 1);
-              if (slot < SLOTS) st_dev(dst + slot, cand_key(et.x[s][w], c * TILE + tpos<DT>(s, w)));
-              else over = true;
+              if (slot < SLOTS) sm.keys[slot] = cand_key(et.x[s][w], c * TILE + tpos<DT>(s, w));
             }
           }
         }
@@ -1047,8 +1044,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
     };
     if (lim >= TILE) walk(std::true_type());
     else walk(std::false_type());
-    if (over) st_dev(P.ovf + item, 1);
   }
+  // wave 0 publishes the record and the candidates (one store for all of
+  // them), so the other waves of a tile that does not merge are done here
+  __syncthreads();
+  if (wid != 0 && c != P.nT - 1) return;
 
   // the tile record (wave 0: lanes 0-7 write one word each)
   if (wid == 0) {
@@ -1073,8 +1073,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
       else word = ((uint64_t)sm.w8[2 * (lane - 4) + 1] << 32) | sm.w8[2 * (lane - 4)];
       st_dev((uint64_t *)(P.recs + item) + lane, word);
     }
+    const int nc = sm.bc[0];
+    if (lane < SLOTS && lane < nc) st_dev(P.cand + (int64_t)item * SLOTS + lane, sm.keys[lane]);
+    if (lane == 0 && nc > SLOTS) st_dev(P.ovf + item, 1);
+    stores_done();
   }
-  block_stores_done();
   if (c != P.nT - 1) {                                   // not the group's last tile: announce and leave
     if (tid == 0) add_dev_noret(P.garrive + (int64_t)G.g * CTR, 1);
     return;
