@@ -2,6 +2,7 @@
 function the header declares, sizes its workspace, describes its error codes
 and rejects bad arguments on the host before anything is enqueued."""
 import ctypes
+import os
 
 import pytest
 
@@ -146,3 +147,26 @@ def test_product_path_never_touches_the_oracle():
         text = open(f).read()
         assert "import oracle" not in text and "sv_oracle" not in text and "orc_verify" not in text, f
         assert "kd_oracle" not in text, f
+
+
+def test_dispatch_table_matches_its_measurement():
+    """The layout table compiled into the library is the one its committed
+    measurement chose: every row of the timing table (the faster layout per
+    dtype, mode, B, k) has the same entry in sv_dispatch.h, in the same order."""
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = open(os.path.join(root, "draft_verification_spec_amd", "csrc", "sv_dispatch.h")).read()
+    entries = [tuple(int(v) for v in m) for m in
+               re.findall(r"\{(-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+)\}", hdr)]
+    assert entries[-1] == (0, 0, -1, -1, 0)                    # end marker
+    rows = []
+    for line in open(os.path.join(root, "profiles", "dispatch_layout_V151936.md")):
+        p = [x.strip() for x in line.strip().strip("|").split("|")]
+        if len(p) != 7 or p[0] not in ("bf16", "f32"):
+            continue
+        launch, xcd = float(p[4]), float(p[5])
+        lay = sv.SV_LAYOUT_LAUNCH if p[6] == "launch" else sv.SV_LAYOUT_XCD_RUNS
+        # the faster of the two (the timings are printed to 0.01 us: equal ones are a tie)
+        assert (launch <= xcd) if lay == sv.SV_LAYOUT_LAUNCH else (xcd <= launch), line
+        rows.append((int(p[2]), int(p[3]), 1 if p[0] == "bf16" else 0, 1 if p[1] == "greedy" else 0, lay))
+    assert rows and rows == entries[:-1]
