@@ -23,7 +23,8 @@ SV_F32, SV_BF16 = 0, 1
 TOPK = 32
 SV_OK = 0
 SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_TEMPERATURE, SV_ERR_DTYPE = -1, -2, -3, -4
-SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_DEVICE = -5, -6, -7
+SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_DEVICE, SV_ERR_SCRATCH = -5, -6, -7, -8
+SV_NOALLOC_MAX_BYTES = 8 << 20
 STATUS_BAD_TOKEN, STATUS_NAN, STATUS_POSINF, STATUS_EMPTY_ROW = 1, 2, 4, 8
 STATUS_BAD_UNIFORM, STATUS_SYNC_TIMEOUT = 16, 32
 
@@ -78,6 +79,9 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify.argtypes = [ctypes.POINTER(sv_shape_t), P, P, P, P, P, P, P, P,
                                     ctypes.POINTER(sv_aux_t), P, ctypes.c_size_t, P]
         lib.spec_verify.restype = ctypes.c_int
+        lib.spec_verify_noalloc.argtypes = [ctypes.POINTER(sv_shape_t), P, P, P, P, P, P, P, P,
+                                            ctypes.POINTER(sv_aux_t), P]
+        lib.spec_verify_noalloc.restype = ctypes.c_int
         lib.sv_kd_workspace_bytes.argtypes = [ctypes.POINTER(sv_kd_shape_t)]
         lib.sv_kd_workspace_bytes.restype = ctypes.c_size_t
         lib.sv_kd.argtypes = [ctypes.POINTER(sv_kd_shape_t), P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -121,6 +125,16 @@ def spec_verify(shape: Optional[sv_shape_t], target_logits, draft_logits, draft_
                                           accepted_len, out_tokens, topk_val, topk_idx,
                                           None if aux is None else ctypes.byref(aux),
                                           workspace, int(workspace_bytes), stream))
+
+
+def spec_verify_noalloc(shape: Optional[sv_shape_t], target_logits, draft_logits, draft_tokens, uniforms,
+                        accepted_len, out_tokens, topk_val, topk_idx, aux: Optional[sv_aux_t], stream) -> int:
+    """Direct call of the no-allocation C entry point (the library's static
+    scratch in place of a workspace) with raw device addresses (ints or None)."""
+    return int(load_library().spec_verify_noalloc(None if shape is None else ctypes.byref(shape),
+                                                  target_logits, draft_logits, draft_tokens, uniforms,
+                                                  accepted_len, out_tokens, topk_val, topk_idx,
+                                                  None if aux is None else ctypes.byref(aux), stream))
 
 
 # ------------------------------------------------------------ torch front end

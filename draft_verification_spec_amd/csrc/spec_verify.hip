@@ -63,6 +63,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "spec_verify.h"
@@ -1184,14 +1185,51 @@ extern "C" const char *spec_verify_error_string(int code) {
     case SV_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than spec_verify_workspace_bytes";
     case SV_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case SV_ERR_DEVICE: return "current device is not usable";
+    case SV_ERR_SCRATCH:
+      return "spec_verify_noalloc: the shape needs more workspace than its static scratch (SV_NOALLOC_MAX_BYTES, "
+             "8 MiB); call spec_verify with a workspace instead";
     default: return "unknown error code";
   }
 }
 
-extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, const void *draft_logits,
-                           const int32_t *draft_tokens, const float *uniforms, int32_t *accepted_len,
-                           int32_t *out_tokens, float *topk_val, int32_t *topk_idx, const sv_aux_t *aux,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+// ---------------------------------------------------------------- no-allocation entry
+// The workspace of spec_verify_noalloc: one copy of this array per GPU, held
+// until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[SV_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SV_OK;
+}
+
+// Zero n16 16-byte words with vector stores.
+__global__ __launch_bounds__(256) void sv_zero_fill(u32x4 *p, size_t n16) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) p[i] = z;
+}
+
+// Both entry points: validation, then (noalloc) the scratch clear, then the launch.
+int verify_impl(const sv_shape_t *shape, const void *target_logits, const void *draft_logits,
+                const int32_t *draft_tokens, const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
+                float *topk_val, int32_t *topk_idx, const sv_aux_t *aux, void *workspace, size_t workspace_bytes,
+                void *stream, bool noalloc) {
   if (!shape) return SV_ERR_NULL;
   const sv_shape_t s = *shape;
   if (s.dtype != SV_F32 && s.dtype != SV_BF16) return SV_ERR_DTYPE;
@@ -1213,6 +1251,17 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   if (s.k > 0 && !draft_tokens) return SV_ERR_NULL;
   if (!greedy && ((s.k > 0 && !draft_logits) || !uniforms)) return SV_ERR_NULL;
   const Layout L = layout_for(s.B, s.k, s.V, s.dtype);
+  if (noalloc) {
+    if (L.total > (size_t)SV_NOALLOC_MAX_BYTES) return SV_ERR_SCRATCH;
+    const int rc = scratch_address(&workspace);
+    if (rc != SV_OK) return rc;
+    workspace_bytes = SV_NOALLOC_MAX_BYTES;
+    // the array keeps the last call's contents: clear what this call uses
+    const size_t n16 = L.total / 16;
+    const unsigned g = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+    hipLaunchKernelGGL(sv_zero_fill, dim3(g), dim3(256), 0, (hipStream_t)stream, (u32x4 *)workspace, n16);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+  }
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return SV_ERR_WORKSPACE;
 
   char *ws = (char *)workspace;
@@ -1260,4 +1309,22 @@ extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, c
   const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, (hipStream_t)stream, ev0, ev1)
                                           : launch<SV_F32>(P, greedy, (hipStream_t)stream, ev0, ev1);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int spec_verify(const sv_shape_t *shape, const void *target_logits, const void *draft_logits,
+                           const int32_t *draft_tokens, const float *uniforms, int32_t *accepted_len,
+                           int32_t *out_tokens, float *topk_val, int32_t *topk_idx, const sv_aux_t *aux,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return verify_impl(shape, target_logits, draft_logits, draft_tokens, uniforms, accepted_len, out_tokens, topk_val,
+                     topk_idx, aux, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int spec_verify_noalloc(const sv_shape_t *shape, const void *target_logits, const void *draft_logits,
+                                   const int32_t *draft_tokens, const float *uniforms, int32_t *accepted_len,
+                                   int32_t *out_tokens, float *topk_val, int32_t *topk_idx, const sv_aux_t *aux,
+                                   void *stream) {
+  return verify_impl(shape, target_logits, draft_logits, draft_tokens, uniforms, accepted_len, out_tokens, topk_val,
+                     topk_idx, aux, nullptr, 0, stream, true);
 }

@@ -59,6 +59,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
 #define SV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than spec_verify_workspace_bytes */
 #define SV_ERR_HIP (-6)         /* a HIP runtime call or the kernel launch failed */
 #define SV_ERR_DEVICE (-7)      /* current device is not usable */
+#define SV_ERR_SCRATCH (-8)     /* spec_verify_noalloc: the shape needs more workspace than
+                                   SV_NOALLOC_MAX_BYTES */
 
 /* per-sequence data-error bits written to aux->status (device side) */
 #define SV_STATUS_BAD_TOKEN 1    /* a draft token is outside [0, V) */
@@ -157,6 +159,32 @@ int spec_verify(const sv_shape_t *shape,
                 float *topk_val, int32_t *topk_idx,
                 const sv_aux_t *aux,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size of the static scratch array behind spec_verify_noalloc, per GPU. */
+#define SV_NOALLOC_MAX_BYTES (8u << 20)
+
+/*
+ * spec_verify without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same inputs, outputs, results, errors and stream
+ * semantics as spec_verify; it calls no hipMalloc, hipFree or other allocating
+ * routine.  Its workspace is a static device array of SV_NOALLOC_MAX_BYTES
+ * (8 MiB) inside the library: each GPU the library runs on holds its own copy
+ * until the process ends, and the first call on a device looks up that copy's
+ * address.  Every call enqueues a small fill kernel that zeroes the part of the
+ * array its shape uses, then the verification kernel, both on `stream`.
+ * Limit: shapes whose spec_verify_workspace_bytes exceeds SV_NOALLOC_MAX_BYTES
+ * return SV_ERR_SCRATCH before anything is enqueued (every workload of up to
+ * B = 32, k = 15, V = 151936 fits; so does B = 256, k = 3, V = 128256).
+ * All calls on one GPU share the one array: calls that overlap in time on the
+ * same GPU (other streams, other host threads) race and must not be made.
+ */
+int spec_verify_noalloc(const sv_shape_t *shape,
+                        const void *target_logits, const void *draft_logits,
+                        const int32_t *draft_tokens, const float *uniforms,
+                        int32_t *accepted_len, int32_t *out_tokens,
+                        float *topk_val, int32_t *topk_idx,
+                        const sv_aux_t *aux, void *stream);
 
 /* Static description of a return code. */
 const char *spec_verify_error_string(int code);

@@ -17,13 +17,13 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = sv.declared_functions()
     assert set(names) == {"spec_verify", "spec_verify_workspace_bytes", "spec_verify_error_string",
-                          "spec_verify_layout_choice", "sv_kd", "sv_kd_workspace_bytes"}
+                          "spec_verify_layout_choice", "spec_verify_noalloc", "sv_kd", "sv_kd_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_error_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = sv.spec_verify_error_string(code)
         assert s and "unknown" not in s
     assert "unknown" in sv.spec_verify_error_string(-99)
