@@ -50,7 +50,7 @@ class sv_kd_shape_t(ctypes.Structure):
                 ("w_max", ctypes.c_float)]
 
 
-KD_BAD_INDEX, KD_NAN, KD_POSINF, KD_EMPTY, KD_SYNC_TIMEOUT = 1, 2, 4, 8, 32
+KD_BAD_INDEX, KD_NAN, KD_POSINF, KD_EMPTY, KD_DUP_INDEX, KD_SYNC_TIMEOUT = 1, 2, 4, 8, 16, 32
 
 
 class SpecVerifyError(RuntimeError):

@@ -262,6 +262,14 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
     if (!pad && (x < 0 || x >= P.V)) F |= SV_KD_BAD_INDEX;
     if (lane < KTOP && !(v == v)) F |= SV_KD_NAN;
     if (lane < KTOP && v == __builtin_inff()) F |= SV_KD_POSINF;
+    // an in-range id that an earlier non-padding entry already names: the
+    // stored entries are then no distribution over tokens
+    {
+      const int mine = pad ? -1 : x, xs = (!pad && x >= 0 && x < P.V) ? x : -1;
+      bool dup = false;
+      for (int e = 0; e < KTOP; ++e) dup |= e < lane && xs >= 0 && __builtin_amdgcn_readlane(mine, e) == xs;
+      if (dup) F |= SV_KD_DUP_INDEX;
+    }
     F = wave_or(F) | (badw ? SV_KD_BAD_INDEX : 0);
     const bool use = !pad && !F;
     const float Mv = wave_max_f(use ? v : NEG_INF);
@@ -314,8 +322,8 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
   // ---- the gradient of this tile: w * q everywhere, then w * (q - pt) at the
   // stored ids that fall in it.  A patch is written by the thread that wrote
   // the entry's vector, after it in program order, so it lands last without a
-  // wait for the tile's stores; entries go in entry order, so a repeated id
-  // keeps its last one.
+  // wait for the tile's stores (a row's stored ids are distinct: a repeat is a
+  // data error, so no two patches of a row meet).
   if (P.grad) {
     const float hi = (float)lse2, lo = (float)(lse2 - (double)hi);
     const float corr = 1.f - lo * (float)LN2;

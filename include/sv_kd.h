@@ -43,6 +43,7 @@ extern "C" {
 #define SV_KD_NAN 2         /* the drafter row or a stored value holds a NaN */
 #define SV_KD_POSINF 4      /* the drafter row or a stored value holds +inf */
 #define SV_KD_EMPTY 8       /* the drafter row is all -inf, or no stored entry is finite */
+#define SV_KD_DUP_INDEX 16  /* two non-padding stored entries of the row name the same id */
 #define SV_KD_SYNC_TIMEOUT 32 /* internal: a bounded wait gave up or the workspace was not
                                  zero-filled (never expected) */
 
@@ -70,7 +71,9 @@ size_t sv_kd_workspace_bytes(const sv_kd_shape_t *shape);
  *                run fastest
  *   topk_val     [N, 32] fp32 stored target logits; an entry with value -inf
  *                or id -1 is padding (weight 0)
- *   topk_idx     [N, 32] int32 token ids (distinct within a row)
+ *   topk_idx     [N, 32] int32 token ids, distinct within a row (a top-32 lists each
+ *                token once); a row naming one id in two non-padding entries is
+ *                a data error (SV_KD_DUP_INDEX)
  *   row_sample   [N] int32 sample of each row, in [0, S)
  *   rewards      [S] fp32
  * Outputs (device pointers, caller-owned):

@@ -22,16 +22,35 @@ STATUS_BAD_TOKEN, STATUS_NAN, STATUS_POSINF, STATUS_EMPTY_ROW, STATUS_BAD_UNIFOR
 TOPK = 32
 
 
-def build() -> str:
-    """Compile the oracle with gcc (plain C99, no fast-math, no FMA contraction)."""
-    tmp = _LIB + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-                           "-shared", "-o", tmp, *_SRCS, "-lm"])
-    os.replace(tmp, _LIB)
-    return _LIB
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(srcs=None, out=None, extra=()) -> str:
+    """Compile the oracle with gcc (plain C99, no fast-math, no FMA contraction).
+    srcs/out: other sources and library path (the tests build altered copies to
+    check that the pins catch them); extra: more gcc flags (sanitizers)."""
+    srcs = list(srcs or _SRCS)
+    out = out or _LIB
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", *CFLAGS, *extra, "-o", tmp, *srcs, "-lm"])
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
+
+
+def bind(path) -> ctypes.CDLL:
+    """Load an oracle library and declare its two entry points."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.orc_verify.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                               P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_verify.restype = ctypes.c_int
+    lib.kd_oracle.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_double, P, P, P, P, P, P, P, P, P, P]
+    lib.kd_oracle.restype = ctypes.c_int
+    return lib
 
 
 def _load():
@@ -39,15 +58,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in _SRCS):
             build()
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        lib.orc_verify.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
-                                   P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
-        lib.orc_verify.restype = ctypes.c_int
-        lib.kd_oracle.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_double, P, P, P, P, P, P, P, P, P, P]
-        lib.kd_oracle.restype = ctypes.c_int
-        _lib = lib
+        _lib = bind(_LIB)
     return _lib
 
 
@@ -99,7 +110,7 @@ def verify_workload(w, aux=True) -> OracleResult:
                   None if w.temperature == 0 else w.uniforms, w.temperature, w.dtype, aux=aux)
 
 
-KD_BAD_INDEX, KD_NAN, KD_POSINF, KD_EMPTY = 1, 2, 4, 8
+KD_BAD_INDEX, KD_NAN, KD_POSINF, KD_EMPTY, KD_DUP_INDEX = 1, 2, 4, 8, 16
 
 
 def kd(logits, topk_val, topk_idx, row_sample, rewards, group, w_max=float("inf"), dtype=0, grad=True) -> OracleResult:

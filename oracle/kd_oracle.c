@@ -20,7 +20,10 @@
  *
  * Readings where the pages are silent (listed in the design notes): both
  * distributions at temperature 1; positions are summed, not averaged; a stored
- * entry with value -inf or id -1 is padding; the clip bound is the caller's.
+ * entry with value -inf or id -1 is padding; the clip bound is the caller's;
+ * the stored ids of a row are distinct (a top-32 lists each token once), so a
+ * row where two non-padding entries name the same id is a data error
+ * (KD_DUP_INDEX): such a row is no distribution over tokens.
  *
  * Everything is fp64; every sum runs sequentially in ascending order.
  */
@@ -36,6 +39,7 @@
 #define KD_NAN 2
 #define KD_POSINF 4
 #define KD_EMPTY 8
+#define KD_DUP_INDEX 16
 
 static double kd_elem(const void *row, int dtype, int64_t x) {
     if (dtype == KD_F32) return (double)((const float *)row)[x];
@@ -100,6 +104,11 @@ int kd_oracle(int N, int V, int dtype, int64_t stride, int S, int group, double 
             if (v[j] != v[j]) est |= KD_NAN;
             else if (v[j] == INFINITY) est |= KD_POSINF;
             if (!pad && (x[j] < 0 || x[j] >= V)) est |= KD_BAD_INDEX;
+        }
+        for (int j = 0; j < KD_TOP; ++j) {
+            if (v[j] == -INFINITY || x[j] == -1 || x[j] < 0 || x[j] >= V) continue;
+            for (int i = 0; i < j; ++i)
+                if (!(v[i] == -INFINITY || x[i] == -1) && x[i] == x[j]) est |= KD_DUP_INDEX;
         }
         const int s = row_sample[n];
         if (s < 0 || s >= S) est |= KD_BAD_INDEX;

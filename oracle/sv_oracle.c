@@ -177,9 +177,10 @@ static int row_has_nan(const void *row, int dtype, int V) {
  *   uniforms[B, k+2]      unused (may be NULL) when temperature == 0
  * outputs:
  *   accepted_len[B], out_tokens[B, k+1], topk_val/topk_idx[B, k+1, 32], status[B]
- *   optional (NULL = skip): lse_target[B, k+1], lse_draft[B, k], p_tok[B, k],
- *   q_tok[B, k], margin_accept[B, k] (NaN where no test ran), margin_cdf[B]
- *   (NaN where no draw ran).
+ *   optional (NULL = skip): lse_target[B, k+1], lse_draft[B, k], p_tok[B, k] and
+ *   q_tok[B, k] (every drafted position, whether or not the chain reached it),
+ *   margin_accept[B, k] (NaN where no test ran), margin_cdf[B] (NaN where no
+ *   draw ran).
  * Returns 0, or -1 for bad arguments.
  */
 int orc_verify(int B, int k, int V, int dtype, float temperature,
@@ -237,13 +238,16 @@ int orc_verify(int B, int k, int V, int dtype, float temperature,
             for (int i = 0; i < k; ++i)
                 if (lse_draft) lse_draft[(size_t)b * k + i] = st[K1 + i].m / T + log(st[K1 + i].s);
             if (!flags) {
+                /* p_i(x_i) and q_i(x_i) of every drafted position */
+                for (int i = 0; i < k; ++i) {
+                    if (p_tok) p_tok[(size_t)b * k + i] = prob(tb + (size_t)i * V * e, dtype, xb[i], st[i], T);
+                    if (q_tok) q_tok[(size_t)b * k + i] = prob(db + (size_t)i * V * e, dtype, xb[i], st[K1 + i], T);
+                }
                 /* acceptance chain: token i survives iff u_i < min(1, p/q) */
                 for (int i = 0; i < k; ++i) {
                     const void *ti = tb + (size_t)i * V * e, *di = db + (size_t)i * V * e;
                     double p = prob(ti, dtype, xb[i], st[i], T);
                     double q = prob(di, dtype, xb[i], st[K1 + i], T);
-                    if (p_tok) p_tok[(size_t)b * k + i] = p;
-                    if (q_tok) q_tok[(size_t)b * k + i] = q;
                     double ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
                     double a = ratio < 1.0 ? ratio : 1.0;
                     double u = (double)ub[i];

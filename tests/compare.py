@@ -55,9 +55,18 @@ def compare_topk(orc, gpu):
 
 
 def rel_err(a, b):
+    """Largest relative difference of b from a.  An entry that is not finite on
+    one side must be the same non-finite value on the other (NaN with NaN, an
+    infinity with the same infinity); any other pairing is an infinite error."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
-    ok = np.isfinite(a) & np.isfinite(b)
-    if not ok.any():
+    fa, fb = np.isfinite(a), np.isfinite(b)
+    if not np.array_equal(fa, fb):
+        return float("inf")
+    nf = ~fa
+    if not (np.array_equal(np.isnan(a[nf]), np.isnan(b[nf])) and
+            np.array_equal(a[nf][~np.isnan(a[nf])], b[nf][~np.isnan(b[nf])])):
+        return float("inf")
+    if not fa.any():
         return 0.0
-    return float(np.max(np.abs(a[ok] - b[ok]) / np.maximum(np.abs(a[ok]), 1e-300)))
+    return float(np.max(np.abs(a[fa] - b[fa]) / np.maximum(np.abs(a[fa]), 1e-300)))

@@ -47,12 +47,12 @@ def run_gpu(sv, w, aux=True):
     return gpu_to_numpy(r)
 
 
-def check_parity(orc_res, gpu, w, exceptions_budget=True):
+def check_parity(orc_res, gpu, w):
     k = w.k
     rep = compare_decisions(orc_res, gpu, k)
     assert not rep["fails"], rep["fails"][:5]
-    if exceptions_budget:
-        assert rep["exc_pos"] <= 0.001 * rep["positions"], rep
+    # flagged exceptions: under 0.1% of the call's positions B(k+1)
+    assert rep["exc_pos"] <= 0.001 * rep["positions"], rep
     bad_idx, vals_ok = compare_topk(orc_res, gpu)
     assert len(bad_idx) == 0, bad_idx[:5]
     assert vals_ok
@@ -105,15 +105,12 @@ def test_steady_small_batch_full_vocab(sv, orc):
     check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
 
 
-def test_steady_full_size_sampled(sv, orc):
-    """Full B=32 batch in one launch; the oracle recomputes 8 sequences."""
+def test_steady_full_size(sv, orc):
+    """The whole B=32 headline batch in one launch against the oracle."""
     w = sv_inputs.steady()
     g = run_gpu(sv, w)
-    bs = np.array([0, 5, 11, 16, 21, 26, 30, 31])
-    ws = w.subset(bs)
-    o = orc.verify_workload(ws)
-    gs = {k: (v[bs] if v is not None else None) for k, v in g.items()}
-    check_parity(o, gs, ws, exceptions_budget=False)
+    rep = check_parity(orc.verify_workload(w), g, w)
+    log(f"steady: exceptions {rep['exc_pos']} of {rep['positions']} positions")
     assert (g["status"] == 0).all()
     assert ((g["accepted_len"] >= 0) & (g["accepted_len"] <= 3)).all()
 
@@ -121,29 +118,25 @@ def test_steady_full_size_sampled(sv, orc):
 @pytest.mark.parametrize("B", [1, 2, 4])
 def test_longtail(sv, orc, B):
     w = sv_inputs.longtail(B)
-    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
 
 
-def test_grpo_full_size_sampled(sv, orc):
+def test_grpo_full_size(sv, orc):
+    """All 256 sequences of the GRPO batch against the oracle."""
     w = sv_inputs.grpo()
     g = run_gpu(sv, w)
-    bs = np.array([0, 1, 7, 8, 100, 200, 254, 255])
-    ws = w.subset(bs)
-    o = orc.verify_workload(ws)
-    gs = {k: (v[bs] if v is not None else None) for k, v in g.items()}
-    check_parity(o, gs, ws, exceptions_budget=False)
+    rep = check_parity(orc.verify_workload(w), g, w)
+    log(f"grpo: exceptions {rep['exc_pos']} of {rep['positions']} positions")
     # rollouts of one prompt share target row 0: identical top-32 there
     assert np.array_equal(g["topk_idx"][0, 0], g["topk_idx"][7, 0])
 
 
-def test_wide_sampling_sampled(sv, orc):
+def test_wide_sampling_full_size(sv, orc):
+    """All 32 sequences (512 verified rows, fp32) against the oracle."""
     w = sv_inputs.wide()
     g = run_gpu(sv, w)
-    bs = np.array([0, 13, 31])
-    ws = w.subset(bs)
-    o = orc.verify_workload(ws)
-    gs = {k: (v[bs] if v is not None else None) for k, v in g.items()}
-    check_parity(o, gs, ws, exceptions_budget=False)
+    rep = check_parity(orc.verify_workload(w), g, w)
+    log(f"wide: exceptions {rep['exc_pos']} of {rep['positions']} positions")
 
 
 def test_wide_greedy_bit_exact(sv, orc):
@@ -179,7 +172,7 @@ def test_greedy_bf16_prefix_matches(sv, orc):
 @pytest.mark.parametrize("dtype", [sv_inputs.F32, sv_inputs.BF16])
 def test_vocab_edges(sv, orc, V, dtype):
     w = sv_inputs.make_workload("edge", 6, 2, V, dtype, 1.0, 1400 + V, 2.0, 0.7)
-    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
     wg = sv_inputs.make_workload("edge_greedy", 6, 2, V, dtype, 0.0, 1400 + V, 2.0, 0.7, draft_T=0.0)
     o, g = orc.verify_workload(wg), run_gpu(sv, wg)
     for key in ("accepted_len", "out_tokens", "topk_idx"):
@@ -189,7 +182,7 @@ def test_vocab_edges(sv, orc, V, dtype):
 @pytest.mark.parametrize("T", [0.0, 1.0])
 def test_k_zero(sv, orc, T):
     w = sv_inputs.make_workload("k0", 5, 0, 9000, sv_inputs.BF16, T, 1501, 2.0, 0.5)
-    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
 
 
 @pytest.mark.parametrize("dtype", [sv_inputs.BF16, sv_inputs.F32])
@@ -209,7 +202,7 @@ def test_bonus_draw_tile_edges(sv, orc, dtype):
     w.draft = w.target[:, :k].copy()              # p = q: every draft accepted
     o, g = orc.verify_workload(w), run_gpu(sv, w)
     assert (o["accepted_len"] == k).all()
-    check_parity(o, g, w, exceptions_budget=False)
+    check_parity(o, g, w)
 
 
 @pytest.mark.parametrize("which", ["steady", "greedy"])
@@ -230,24 +223,43 @@ def test_layouts_give_identical_results(sv, which):
                 np.testing.assert_array_equal(v, other[key], err_msg=key)
 
 
+@pytest.mark.parametrize("k", [70, 260])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_long_drafts(sv, orc, k, T):
+    """k = 70: more drafts than a wave has lanes, so the draws learn the drawing
+    row from the sequence's assembly; k = 260: k + 2 > 256 entries, so the
+    assembly walks the group records in several rounds.  High acceptance
+    (draft noise 0.05) so that chains run deep."""
+    w = sv_inputs.make_workload("long_k", 3, k, 700, sv_inputs.BF16, T, 2300 + k, 2.0, 0.05,
+                                draft_T=0.0 if T == 0 else None)
+    o = orc.verify_workload(w)
+    g = run_gpu(sv, w, aux=T > 0)
+    if T > 0:
+        check_parity(o, g, w)
+        log(f"long drafts k={k}: accepted {g['accepted_len'].tolist()}")
+    else:
+        for key in ("accepted_len", "out_tokens", "status", "topk_idx"):
+            np.testing.assert_array_equal(o[key], g[key], err_msg=key)
+
+
 def test_plain_full_vocabulary(sv, orc):
     """k = 0 at the pages' vocabulary: plain temperature sampling (bonus draws
     only) with the top-32, in the plain bench workload's distribution."""
     w = sv_inputs.plain(B=8)
-    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
 
 
 @pytest.mark.parametrize("dtype,V", [(sv_inputs.BF16, 128 * 4096), (sv_inputs.F32, 128 * 2048)])
 def test_largest_vocab(sv, orc, dtype, V):
     """The largest vocabulary the library takes: 64 tiles of 16 KB per row."""
     w = sv_inputs.make_workload("maxV", 1, 1, V, dtype, 1.0, 1601, 3.0, 1.0)
-    check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+    check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
 
 
 def test_temperatures(sv, orc):
     for T in (0.25, 0.7, 2.0):
         w = sv_inputs.make_workload("temp", 8, 3, 20000, sv_inputs.F32, T, 1701, 3.0, 1.0)
-        check_parity(orc.verify_workload(w), run_gpu(sv, w), w, exceptions_budget=False)
+        check_parity(orc.verify_workload(w), run_gpu(sv, w), w)
 
 
 def test_top32_ties_and_constant_rows(sv, orc):
@@ -300,7 +312,7 @@ def test_strided_and_unaligned_rows(sv, orc):
     for key in ("accepted_len", "out_tokens", "topk_idx", "topk_val", "p_tok", "lse_target"):
         np.testing.assert_array_equal(base[key], g[key], err_msg=key)
     # V=10001 bf16 rows start at odd 16-byte phases: the element-wise load path
-    check_parity(orc.verify_workload(w), base, w, exceptions_budget=False)
+    check_parity(orc.verify_workload(w), base, w)
 
 
 # ------------------------------------------------------------------ determinism
@@ -339,7 +351,7 @@ def test_workspace_left_zero_for_any_next_shape(sv, orc):
         r = sv.verify(t, d, x, u, w.temperature, aux=True, workspace=ws)
         torch.cuda.synchronize()
         assert int(ws.count_nonzero().item()) == 0
-        check_parity(orc.verify_workload(w), gpu_to_numpy(r), w, exceptions_budget=False)
+        check_parity(orc.verify_workload(w), gpu_to_numpy(r), w)
     wg = sv_inputs.wide(seed=2205, B=3, k=4, V=30000, greedy=True)
     t, _, x, _ = sv.to_device(wg)
     sv.verify(t, None, x, None, 0.0, workspace=ws)

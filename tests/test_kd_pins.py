@@ -117,25 +117,27 @@ def test_clip_and_empty_group(oracle_mod):
 
 def test_error_rows(oracle_mod):
     z, tv, ti = _row_with_kl(0.3)
-    Z = np.stack([z] * 6)
-    TV = np.stack([tv] * 6)
-    TI = np.stack([ti] * 6)
+    Z = np.stack([z] * 7)
+    TV = np.stack([tv] * 7)
+    TI = np.stack([ti] * 7)
     Z[0, 5] = np.nan                              # NaN drafter logit
     TI[1, 3] = 64                                 # stored id out of range
     Z[2, :] = -np.inf                             # empty drafter row
     TV[3, :] = -np.inf                            # no stored entry
     TV[4, 3] = np.inf                             # +inf stored value
-    rs = np.array([0, 0, 0, 0, 0, 7], np.int32)   # row 5: sample id out of range
+    rs = np.array([0, 0, 0, 0, 0, 7, 0], np.int32)   # row 5: sample id out of range
+    TI[6, 20] = TI[6, 4]                          # row 6: one id in two stored entries
     r = oracle_mod.kd(Z, TV, TI, rs, np.ones(2, np.float32), group=2)
     K = oracle_mod
     np.testing.assert_array_equal(r.status, [K.KD_NAN, K.KD_BAD_INDEX, K.KD_EMPTY, K.KD_EMPTY, K.KD_POSINF,
-                                             K.KD_BAD_INDEX])
+                                             K.KD_BAD_INDEX, K.KD_DUP_INDEX])
     assert np.all(np.isnan(r.kl)) and r.loss == 0.0 and not r.grad.any()
     # padding entries (value -inf or id -1) carry no weight and are no error
     TV2 = tv.copy()
     TI2 = ti.copy()
     TV2[5] = -np.inf
     TI2[6] = -1
+    TI2[5] = TI2[7]                               # a padding entry may repeat a used id
     r2 = oracle_mod.kd(z[None], TV2[None], TI2[None], np.zeros(1, np.int32), np.ones(1, np.float32), group=1)
     used = np.ones(32, bool)
     used[[5, 6]] = False
