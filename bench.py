@@ -7,14 +7,19 @@ seeded; 16 copies of the batch (1.09 GB, over four times the 256 MB Infinity
 Cache) rotate so every step reads its logits from HBM.
 
 Prints one JSON line.  value = algorithmic logit bytes (each logit read once,
-B(2k+1)V * 2 bytes) / wall time per step, inputs resident in HBM.  roofline =
-the same bytes / the duration of the one kernel launch sv_verify (streaming,
-merges, assembly and draw; HIP events the library records right before and
-after it on the launch stream), against the 8 TB/s HBM peak.  cpu_baseline =
-the plain C oracle on the host over a bounded number of whole batches.
+B(2k+1)V * 2 bytes) / wall time per step over K back-to-back steps, inputs
+resident in HBM.  By default the K calls are replayed from a HIP graph (one
+capture of one call per input copy), so the host's per-call cost stays out of
+the number, as in a serving loop that captures its step; --eager times K
+direct calls instead.  roofline = the same bytes / the mean duration of the
+kernel launch (torch events recorded on the launch stream right before and
+after each of K direct calls; a call is that one launch), against the 8 TB/s
+HBM peak.  cpu_baseline = the plain C oracle on the host over a bounded number
+of whole batches.
 
-  python bench.py [--steps K] [--warmup W] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|plain|tiny]
+  python bench.py [--steps K] [--warmup W] [--eager] [--workload steady|longtail1|longtail2|longtail4|grpo|wide|wide_greedy|plain|tiny]
   python bench.py --workload kd   # the drafter distillation step over the stored top-32 (its own metric)
+  python bench.py --stream-read   # a plain HBM read of the steady batch's bytes: the achievable read rate
   python bench.py --copy-calib    # a plain 1 GiB device copy, for HBM counter calibration
   python bench.py --source-hash sv_verify|sv_kd_kernel   # the source hash a profile summary records
 """
@@ -207,13 +212,74 @@ def bench_kd(args):
         sample_bytes = len(rows) * w.V * (w.elem_bytes + 2)
         g_kl = kl.cpu().numpy()[rows]
         ok = o_status == 0
+        model, nthreads, usable = host_cpu()
         line["cpu_baseline"] = {
             "value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"all {len(rows)} rows of the batch (loss and fp64 gradient), {dt:.2f} s, single thread of "
-                      f"{os.cpu_count()} host threads", "rows_per_s": round(len(rows) / dt, 2)}
+            "sample": f"all {len(rows)} rows of the batch (loss and fp64 gradient), {dt:.2f} s, one thread",
+            "cpu_model": model, "host_threads": nthreads, "usable_threads": usable,
+            "rows_per_s": round(len(rows) / dt, 2)}
         line["parity_vs_oracle"] = {"rows": int(len(rows)), "max_abs_kl_err": float(np.max(np.abs(g_kl[ok] - o_kl[ok]))),
                                     "status_equal": bool(np.array_equal(st.cpu().numpy()[rows], o_status))}
     print(json.dumps(line), flush=True)
+
+
+def host_cpu():
+    """CPU model and thread counts of this host, for the baseline's context."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return model, os.cpu_count(), usable
+
+
+def bench_stream_read(args):
+    """The achievable HBM read rate: a kernel that only reads (16-byte loads,
+    256 threads, each workgroup issuing all its loads at once, chunks of 32 KB
+    as a pair tile of the verification kernel), over the steady batch's 68 MB
+    per launch, 16 rotating copies (over 4x the Infinity Cache)."""
+    import ctypes
+    import torch
+    from draft_verification_spec_amd import _build
+    lib = ctypes.CDLL(_build.STREAM_LIB)
+    lib.sv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sv_stream_read.restype = ctypes.c_int
+    vecs = 8
+    chunk = 256 * 16 * vecs
+    nbytes = (68067328 // chunk) * chunk
+    copies = args.copies or max(1, -(-4 * MALL_BYTES // nbytes))
+    bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(nbytes // chunk, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        rc = lib.sv_stream_read(bufs[i % copies].data_ptr(), nbytes, vecs, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"sv_stream_read failed: {rc}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    print(json.dumps({
+        "metric": "stream-read GB/s (achievable HBM read rate)", "value": round(nbytes / (us.mean() * 1e-6) / 1e9, 1),
+        "unit": "GB/s", "bytes_per_launch": nbytes, "chunk_bytes": chunk, "workgroups": nbytes // chunk,
+        "input_copies_rotated": copies, "steps": args.steps, "kernel_us_mean": round(float(us.mean()), 3),
+        "kernel_us_p10_p50_p90": [round(float(np.percentile(us, q)), 3) for q in (10, 50, 90)],
+        "frac_of_8TBs": round(nbytes / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
 def main():
@@ -223,8 +289,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="steady")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: enough for 4x the MALL)")
+    ap.add_argument("--eager", action="store_true", help="time K direct calls instead of HIP-graph replays")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--stream-read", action="store_true")
     ap.add_argument("--source-hash", default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -236,6 +304,8 @@ def main():
         return
     if args.copy_calib:
         return copy_calib()
+    if args.stream_read:
+        return bench_stream_read(args)
     if args.workload in ("kd", "kd_small"):
         return bench_kd(args)
 
@@ -250,53 +320,93 @@ def main():
     copies = args.copies or max(1, -(-4 * MALL_BYTES // alg))
     sets = [(t, d, x, u)] + [(t.clone(), d.clone(), x.clone(), u.clone()) for _ in range(copies - 1)]
     shape = sv.make_shape(w.B, w.k, w.V, w.dtype, w.temperature)
-    ws = sv.workspace_for(t.device, sv.spec_verify_workspace_bytes(shape))
-    stream = torch.cuda.current_stream()
+    dev = t.device
+    ws = torch.zeros(max(sv.spec_verify_workspace_bytes(shape), 256), dtype=torch.uint8, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    acc = torch.empty(w.B, **i32)
+    out = torch.empty(w.B, w.k + 1, **i32)
+    tv = torch.empty(w.B, w.k + 1, sv.TOPK, dtype=torch.float32, device=dev)
+    ti = torch.empty(w.B, w.k + 1, sv.TOPK, **i32)
+    st = torch.empty(w.B, **i32)
+    aux = sv.sv_aux_t(st.data_ptr(), None, None, None, None, sv.SV_LAYOUT_AUTO)
+    torch.cuda.synchronize()
 
-    def step(i, events=None):
+    def call(i, stream):
         tt, dd, xx, uu = sets[i % copies]
-        return sv.verify(tt, None if greedy else dd, xx, None if greedy else uu, w.temperature,
-                         workspace=ws, stream=stream.cuda_stream, events=events)
+        rc = sv.spec_verify(shape, tt.data_ptr(), None if greedy else dd.data_ptr(),
+                            xx.data_ptr() if w.k > 0 else None, None if greedy else uu.data_ptr(),
+                            acc.data_ptr(), out.data_ptr(), tv.data_ptr(), ti.data_ptr(), aux,
+                            ws.data_ptr(), ws.numel(), stream)
+        if rc != sv.SV_OK:
+            raise sv.SpecVerifyError(rc)
 
+    stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        step(i)
+        call(i, stream.cuda_stream)
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps over {copies} input copies",
           file=sys.stderr, flush=True)
 
-    # kernel duration: the library records an event pair around its launch on the launch stream
+    # kernel duration: events on the launch stream right before and after each of K direct calls
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev:                      # torch creates the underlying events on first record
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
     for i in range(args.steps):
-        step(args.warmup + i, events=ev[i])
+        ev[i][0].record(stream)
+        call(args.warmup + i, stream.cuda_stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
     # whole-job wall time over K back-to-back steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    last = None
-    for i in range(args.steps):
-        last = step(args.warmup + args.steps + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if args.eager:
+        timing = "eager: K direct calls back to back"
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            call(args.warmup + args.steps + i, stream.cuda_stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        # one graph of one call per input copy (and one for the remainder), captured on a side stream
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream().cuda_stream
+                for i in range(n):
+                    call(i, cs)
+            return g
+        full, rest = divmod(args.steps, copies)
+        g_full = capture(copies) if full else None
+        g_rest = capture(rest) if rest else None
+        torch.cuda.synchronize()
+        if g_full is not None:
+            g_full.replay()                # one untimed replay
+        torch.cuda.synchronize()
+        timing = f"HIP graph: {copies} calls per replay, {full} replays + {rest} calls"
+        t0 = time.perf_counter()
+        for _ in range(full):
+            g_full.replay()
+        if g_rest is not None:
+            g_rest.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
     rows = w.B * (w.k + 1)
     value = alg / (ms_per_step * 1e-3) / 1e9
     kern_avg = float(kern_ms.mean())
     achieved = alg / (kern_avg * 1e-3) / 1e9
-    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in last._asdict().items()}
+    # the last step's outputs, from the last input copy used
+    call(copies - 1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = dict(accepted_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(), topk_val=tv.cpu().numpy(),
+             topk_idx=ti.cpu().numpy(), status=st.cpu().numpy())
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype else "f32",
         "data": "synthetic (seeded Philox logits of the workload's shape and distribution)",
         "config": {"workload": describe(w), "B": w.B, "k": w.k, "V": w.V, "verified_rows": rows,
-                   "alg_bytes_per_step": alg, "input_copies_rotated": copies},
+                   "alg_bytes_per_step": alg, "input_copies_rotated": copies, "timing": timing},
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -311,13 +421,14 @@ def main():
     if not args.no_cpu:
         dt, n, o = cpu_baseline(w)
         from tests.compare import compare_decisions   # same comparator as the parity tests
-        rep = compare_decisions(o, g, w.k) if not greedy else None
+        model, nthreads, usable = host_cpu()
         line["cpu_baseline"] = {
             "value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full {describe(w)} batch, {n} pass(es), {dt:.2f} s per batch, single thread of "
-                      f"{os.cpu_count()} host threads",
+            "sample": f"the full {describe(w)} batch, {n} pass(es), {dt:.2f} s per batch, one thread",
+            "cpu_model": model, "host_threads": nthreads, "usable_threads": usable,
             "rows_per_s": round(rows / dt, 2)}
-        if rep is not None:
+        if not greedy:
+            rep = compare_decisions(o, g, w.k)
             line["parity_vs_oracle"] = {"fails": len(rep["fails"]), "exception_positions": rep["exc_pos"],
                                         "positions": rep["positions"]}
         else:

@@ -37,8 +37,7 @@ class sv_shape_t(ctypes.Structure):
 
 class sv_aux_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_void_p), ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p),
-                ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p),
-                ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p), ("item_layout", ctypes.c_int32)]
+                ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p), ("item_layout", ctypes.c_int32)]
 
 
 SV_LAYOUT_AUTO, SV_LAYOUT_LAUNCH, SV_LAYOUT_XCD_RUNS = 0, 1, 2
@@ -144,15 +143,30 @@ _workspaces = {}
 
 
 def workspace_for(device, nbytes: int):
-    """A zero-filled per-device workspace of at least nbytes (reused: every call
-    leaves it zero-filled).  Calls on different streams sharing it must not overlap."""
+    """A zero-filled per-device workspace of at least nbytes (reused: every
+    successful call leaves it zero-filled).  A new workspace is zero-filled and
+    the filling stream synchronised before it is returned, so a launch on any
+    stream finds it zero.  Calls on different streams sharing it must not
+    overlap.  After a call reports STATUS_SYNC_TIMEOUT (or KD_SYNC_TIMEOUT)
+    the workspace may hold leftovers: call reset_workspaces() before reusing it."""
     import torch
     key = torch.device(device).index
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        torch.cuda.current_stream(ws.device).synchronize()
         _workspaces[key] = ws
     return ws
+
+
+def reset_workspaces():
+    """Zero every cached workspace again (after a SYNC_TIMEOUT status), waiting
+    for all work on their devices first."""
+    import torch
+    for ws in _workspaces.values():
+        torch.cuda.synchronize(ws.device)
+        ws.zero_()
+        torch.cuda.synchronize(ws.device)
 
 
 def _row_stride(t, rows_per_seq):
@@ -174,9 +188,10 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bo
     target [B,k+1,V] and draft [B,k,V] (float32 or bfloat16, same dtype; draft
     may be None when temperature == 0), draft_tokens [B,k] int32, uniforms
     [B,k+2] float32 (None allowed when temperature == 0).  events: optional
-    pair of torch.cuda.Event recorded right before and after the kernel on
-    the launch stream.  layout: SV_LAYOUT_* order of the streaming items
-    (results do not depend on it).  Returns device tensors.
+    pair of torch.cuda.Event recorded on the current stream right before and
+    after the call (the launch must then be on the current stream).  layout:
+    SV_LAYOUT_* order of the streaming items (results do not depend on it).
+    Returns device tensors.
     """
     import torch
     if target.dim() != 3:
@@ -221,25 +236,29 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bo
     tv = torch.empty(B, K1, TOPK, **f32)
     ti = torch.empty(B, K1, TOPK, **i32)
     st = torch.empty(B, **i32)
-    a = sv_aux_t(st.data_ptr(), None, None, None, None, None, None, int(layout))
+    a = sv_aux_t(st.data_ptr(), None, None, None, None, int(layout))
     lt = ld = pt = qt = None
     if aux and not greedy:
         lt = torch.empty(B, K1, **f32)
         ld = torch.empty(B, k, **f32)
         pt = torch.empty(B, k, **f32)
         qt = torch.empty(B, k, **f32)
-        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr(), None, None,
-                     int(layout))
-    if events is not None:
-        a.event_begin, a.event_end = events[0].cuda_event, events[1].cuda_event
+        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr(), int(layout))
     nbytes = spec_verify_workspace_bytes(shape)
     ws = workspace if workspace is not None else workspace_for(dev, nbytes)
+    cur = torch.cuda.current_stream(dev)
     if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = cur.cuda_stream
+    if events is not None:
+        if stream != cur.cuda_stream:
+            raise ValueError("events are recorded on the current stream: launch there")
+        events[0].record(cur)
     rc = spec_verify(shape, target.data_ptr(), None if greedy else draft.data_ptr(),
                      draft_tokens.data_ptr() if k > 0 else None, None if greedy else uniforms.data_ptr(),
                      acc.data_ptr(), out.data_ptr(), tv.data_ptr(), ti.data_ptr(), a,
                      ws.data_ptr(), ws.numel(), stream)
+    if events is not None:
+        events[1].record(cur)
     if rc != SV_OK:
         raise SpecVerifyError(rc)
     return Result(acc, out, tv, ti, st, lt, ld, pt, qt)

@@ -1127,16 +1127,12 @@ bool shape_ok(const sv_shape_t *s) {
 }
 
 template <int DT>
-hipError_t launch(const Params &P, bool greedy, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
   // streaming workgroups, then (sampling) one draw workgroup per (sequence, tile)
   const unsigned grid = (unsigned)P.items + (greedy ? 0u : (unsigned)P.B * (unsigned)P.nT);
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipErrorInvalidValue;
   if (greedy) hipLaunchKernelGGL((sv_verify<DT, true>), dim3(grid), dim3(TPB), 0, stream, P);
   else hipLaunchKernelGGL((sv_verify<DT, false>), dim3(grid), dim3(TPB), 0, stream, P);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return hipErrorInvalidValue;
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 // The item layout for a shape.  In launch order, tile c of every group goes
@@ -1304,10 +1300,8 @@ int verify_impl(const sv_shape_t *shape, const void *target_logits, const void *
   P.t_vec = (((uintptr_t)target_logits & 15) == 0 && ((ts * esz) & 15) == 0) ? 1 : 0;
   P.d_vec = (!greedy && s.k > 0 && ((uintptr_t)draft_logits & 15) == 0 && ((ds * esz) & 15) == 0) ? 1 : 0;
 
-  const hipEvent_t ev0 = aux ? (hipEvent_t)aux->event_begin : nullptr;
-  const hipEvent_t ev1 = aux ? (hipEvent_t)aux->event_end : nullptr;
-  const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, (hipStream_t)stream, ev0, ev1)
-                                          : launch<SV_F32>(P, greedy, (hipStream_t)stream, ev0, ev1);
+  const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, (hipStream_t)stream)
+                                          : launch<SV_F32>(P, greedy, (hipStream_t)stream);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

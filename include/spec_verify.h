@@ -89,9 +89,6 @@ typedef struct {
     float *lse_draft;    /* [B,k]   ln sum_x exp(d_x / T)   (sampling only) */
     float *p_tok;        /* [B,k]   p_i(x_i)                (sampling only) */
     float *q_tok;        /* [B,k]   q_i(x_i)                (sampling only) */
-    void *event_begin;   /* hipEvent_t recorded on the stream right before the kernel
-                            launch, or NULL */
-    void *event_end;     /* hipEvent_t recorded right after it, or NULL */
     int32_t item_layout; /* order in which the streaming workgroups take the (group, tile)
                             items: SV_LAYOUT_AUTO (0, the library's measured table),
                             SV_LAYOUT_LAUNCH (launch order) or SV_LAYOUT_XCD_RUNS (one
@@ -136,8 +133,13 @@ int spec_verify_layout_choice(const sv_shape_t *shape);
  *   aux           optional outputs; NULL for none
  * Workspace: device memory of at least spec_verify_workspace_bytes(shape)
  *   bytes, 256-byte aligned, zero-filled before its first use.  Every call
- *   leaves it zero-filled again for the next one.  Calls that share a
- *   workspace must not overlap in time.
+ *   whose sequences carry no SV_STATUS_SYNC_TIMEOUT leaves it zero-filled
+ *   again for the next one.  A call that reports SV_STATUS_SYNC_TIMEOUT may
+ *   leave counters and records behind, and it sets a fault word in the
+ *   workspace that is never cleared by the library: every later call on that
+ *   workspace reports SV_STATUS_SYNC_TIMEOUT too, until the caller zero-fills
+ *   the whole workspace again.  Calls that share a workspace must not overlap
+ *   in time.
  * Errors: host-detectable argument errors return a negative SV_ERR_* code
  *   before anything is enqueued.  Data errors (bad token, NaN, +inf, all -inf
  *   row, bad uniform) cannot be seen without a device sync; they set the
@@ -149,6 +151,13 @@ int spec_verify_layout_choice(const sv_shape_t *shape);
  *   assembly); in sampling mode draw workgroups follow (residual or bonus
  *   draw).  A workgroup waits only for workgroups of lower index or for the
  *   other draw workgroups of its sequence, always with a time bound.
+ *   Assumption behind every such wait: the GPU starts the workgroups of a
+ *   launch in index order within each of its XCDs (workgroups are dealt to
+ *   the XCDs round robin), so a waited-for workgroup has started or can start
+ *   once earlier ones finish; nothing in HIP promises this for an ordinary
+ *   launch.  Should a wait still not end, it gives up after 0.2 s, sets
+ *   SV_STATUS_SYNC_TIMEOUT in the sequences assembled after it, and the
+ *   kernel completes (its results are then not to be used).
  * The library allocates no memory and keeps no per-call state; it is safe to
  * call from several host threads with separate workspaces.
  */

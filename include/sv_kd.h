@@ -84,16 +84,22 @@ size_t sv_kd_workspace_bytes(const sv_kd_shape_t *shape);
  *   grad    [N, V] (grad_dtype, row stride V) or NULL; zero rows for rows with
  *           a data error
  * Workspace: at least sv_kd_workspace_bytes(shape) bytes, 256-byte aligned,
- *   zero-filled before its first use; every call leaves it zero-filled again.
- *   Calls that share a workspace must not overlap in time.
+ *   zero-filled before its first use; every call without SV_KD_SYNC_TIMEOUT
+ *   leaves it zero-filled again.  After SV_KD_SYNC_TIMEOUT it may hold
+ *   leftovers and a fault word the library never clears (every later call
+ *   reports SV_KD_SYNC_TIMEOUT) until the caller zero-fills it again.  Calls
+ *   that share a workspace must not overlap in time.
  * Errors: argument errors return a negative SV_ERR_* code before anything is
  *   enqueued.  Data errors set the row's status bits (a row_sample outside
  *   [0, S) counts as SV_KD_BAD_INDEX).
  * N = 0: returns SV_OK, enqueues nothing and leaves every output, loss
  *   included, untouched (the caller sets loss = 0 for an empty batch).
  * Execution: one kernel launch, one workgroup per (row, 16 KB tile).  The
- *   workgroups of a row exchange their tile statistics and wait (bounded) for
- *   one another; they are dispatched together.
+ *   workgroups of a row exchange their tile statistics and wait for one
+ *   another.  Assumption: the GPU starts a launch's workgroups in index order
+ *   within each XCD, so a row's workgroups, which are consecutive, run
+ *   together (nT <= 64 of them); HIP does not promise this for an ordinary
+ *   launch.  Each wait gives up after 0.2 s and sets SV_KD_SYNC_TIMEOUT.
  */
 int sv_kd(const sv_kd_shape_t *shape, const void *draft_logits, const float *topk_val,
           const int32_t *topk_idx, const int32_t *row_sample, const float *rewards,

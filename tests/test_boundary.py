@@ -64,7 +64,7 @@ def test_layout_choice():
                     assert f(sv.make_shape(B, k, 151936, dt, T)) in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS)
     assert f(sv.make_shape(-1, 3, 1000, 0, 1.0)) == 0
     assert f(sv.make_shape(2, 3, 1000, 0, -1.0)) == 0
-    bad = sv.sv_aux_t(None, None, None, None, None, None, None, 3)
+    bad = sv.sv_aux_t(None, None, None, None, None, 3)
     assert _call(sv.make_shape(2, 3, 1000, 0, 1.0), aux=bad) == sv.SV_ERR_SHAPE
 
 

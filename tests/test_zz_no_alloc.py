@@ -39,7 +39,7 @@ def _run(sv, w, noalloc):
     greedy = w.temperature == 0
     o = _outputs(w.B, w.k, t.device)
     aux = sv.sv_aux_t(o["st"].data_ptr(), o["lt"].data_ptr(), o["ld"].data_ptr(), o["pt"].data_ptr(),
-                      o["qt"].data_ptr(), None, None, sv.SV_LAYOUT_AUTO)
+                      o["qt"].data_ptr(), sv.SV_LAYOUT_AUTO)
     shape = sv.make_shape(w.B, w.k, w.V, w.dtype, w.temperature)
     args = (shape, t.data_ptr(), None if greedy else d.data_ptr(), x.data_ptr() if w.k > 0 else None,
             None if greedy else u.data_ptr(), o["acc"].data_ptr(), o["out"].data_ptr(), o["tv"].data_ptr(),
