@@ -251,6 +251,16 @@ __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool ve
   static_assert(!TM || NS == NSEG, "the draw order is defined for NSEG vectors");
   constexpr int E = Fmt<DT>::E, W = Fmt<DT>::W;
   const int64_t c0 = (int64_t)c * (TPB * NS * W);
+  if (vec && c0 + TPB * NS * W <= V) {
+    // the whole tile lies in the row (the usual case): unconditional loads
+    const char *base = row + (c0 + (TM ? dpos<DT>(0, 0) : tpos<DT>(0, 0))) * E;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x4 *a = (const u32x4 *)(base + (int64_t)(TM ? s * W : s * TPB * W) * E);
+      r[s] = NT ? __builtin_nontemporal_load(a) : *a;
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int64_t e0 = c0 + (TM ? dpos<DT>(s, 0) : tpos<DT>(s, 0));
