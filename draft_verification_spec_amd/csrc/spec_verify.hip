@@ -68,7 +68,7 @@
 
 #include "spec_verify.h"
 #include "sv_device.h"
-#include "sv_dispatch.h"
+#include "sv_host.h"
 
 namespace {
 
@@ -1094,37 +1094,15 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
 }
 
 // ---------------------------------------------------------------- host side
-struct Layout {
-  size_t fault, garrive, sarrive, ddone, recs, grec, srec, cand, ovf, dtot, total;
-};
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-int tile_of(int dtype) { return dtype == SV_BF16 ? Fmt<SV_BF16>::TILE : Fmt<SV_F32>::TILE; }
-
-Layout layout_for(int B, int k, int V, int dtype) {
-  const size_t groups = (size_t)B * (k + 1);
-  const size_t nT = ((size_t)V + tile_of(dtype) - 1) / tile_of(dtype);
-  Layout L;
-  size_t o = 0;
-  L.fault = o;   o = align256(o + sizeof(int32_t));     // fixed header, same offset for every shape
-  L.garrive = o; o = align256(o + groups * CTR * sizeof(int32_t));
-  L.sarrive = o; o = align256(o + (size_t)B * CTR * sizeof(int32_t));
-  L.ddone = o;   o = align256(o + (size_t)B * CTR * sizeof(int32_t));
-  L.recs = o;    o = align256(o + groups * nT * sizeof(TileRec));
-  L.grec = o;    o = align256(o + groups * sizeof(GroupRec));
-  L.srec = o;    o = align256(o + (size_t)B * SREC_STRIDE);
-  L.cand = o;    o = align256(o + groups * nT * SLOTS * sizeof(uint64_t));
-  L.ovf = o;     o = align256(o + groups * nT * sizeof(int32_t));
-  L.dtot = o;    o = align256(o + (size_t)B * nT * 2 * sizeof(double));
-  L.total = o;
-  return L;
-}
-
-bool shape_ok(const sv_shape_t *s) {
-  return s->B >= 0 && s->k >= 0 && s->V >= 1 && (s->dtype == SV_F32 || s->dtype == SV_BF16) &&
-         (int64_t)s->V <= (int64_t)MAX_TILES * tile_of(s->dtype);
-}
+using sv_host::Layout;
+using sv_host::layout_for;
+using sv_host::shape_ok;
+using sv_host::table_layout;
+using sv_host::tile_of;
+static_assert(sizeof(TileRec) == sv_host::TILE_REC_BYTES && sizeof(GroupRec) == sv_host::GROUP_REC_BYTES &&
+                  SREC_STRIDE == (int)sv_host::SEQ_REC_BYTES && SLOTS == sv_host::SLOTS && CTR == sv_host::CTR &&
+                  MAX_TILES == sv_host::MAX_TILES && Fmt<SV_BF16>::TILE == 8192 && Fmt<SV_F32>::TILE == 4096,
+              "host layout constants");
 
 template <int DT>
 hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
@@ -1133,28 +1111,6 @@ hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
   if (greedy) hipLaunchKernelGGL((sv_verify<DT, true>), dim3(grid), dim3(TPB), 0, stream, P);
   else hipLaunchKernelGGL((sv_verify<DT, false>), dim3(grid), dim3(TPB), 0, stream, P);
   return hipGetLastError();
-}
-
-// The item layout for a shape.  In launch order, tile c of every group goes
-// to XCD (g * nT + c) mod 8, so with a tile count divisible by 4 the groups'
-// last tiles, which run the merges, crowd onto 2 or 1 of the 8 XCDs (a 16-tile
-// row measured 1.4x slower): XCD runs then.  Otherwise the measured table
-// (taken at 19 bf16 and 38 fp32 tiles): the entry of the same dtype and mode
-// nearest in (log2 B, log2(k + 1)); XCD runs where there is none.
-int table_layout(const sv_shape_t *s) {
-  const int nT = (s->V + tile_of(s->dtype) - 1) / tile_of(s->dtype);
-  if (nT % 4 == 0) return SV_LAYOUT_XCD_RUNS;
-  const bool greedy = s->temperature == 0.f;
-  double best = 1e30;
-  int layout = SV_LAYOUT_XCD_RUNS;
-  for (const SvLayoutEntry *e = kSvLayoutTable; e->dtype >= 0; ++e) {
-    if (e->dtype != s->dtype || e->greedy != (greedy ? 1 : 0)) continue;
-    const double db = log2((double)(s->B > 0 ? s->B : 1)) - log2((double)e->B);
-    const double dk = log2((double)s->k + 1.0) - log2((double)e->k + 1.0);
-    const double d = db * db + dk * dk;
-    if (d < best) { best = d; layout = e->layout; }
-  }
-  return layout;
 }
 
 }  // namespace
@@ -1226,26 +1182,17 @@ int verify_impl(const sv_shape_t *shape, const void *target_logits, const void *
                 const int32_t *draft_tokens, const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
                 float *topk_val, int32_t *topk_idx, const sv_aux_t *aux, void *workspace, size_t workspace_bytes,
                 void *stream, bool noalloc) {
-  if (!shape) return SV_ERR_NULL;
+  bool nothing = false;
+  const int rc0 = sv_host::check_args(shape, target_logits, draft_logits, draft_tokens, uniforms, accepted_len,
+                                      out_tokens, topk_val, topk_idx, aux, &nothing);
+  if (rc0 != SV_OK || nothing) return rc0;
   const sv_shape_t s = *shape;
-  if (s.dtype != SV_F32 && s.dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (!shape_ok(&s)) return SV_ERR_SHAPE;
   const int64_t ts = s.target_row_stride ? s.target_row_stride : s.V;
   const int64_t ds = s.draft_row_stride ? s.draft_row_stride : s.V;
-  if (ts < s.V || ds < s.V) return SV_ERR_SHAPE;
-  const int tile = tile_of(s.dtype);
-  const int64_t nT = ((int64_t)s.V + tile - 1) / tile;
+  const int64_t nT = ((int64_t)s.V + tile_of(s.dtype) - 1) / tile_of(s.dtype);
   const int64_t items = (int64_t)s.B * (s.k + 1) * nT;
-  if (items + (int64_t)s.B * nT > 0x7fffffffLL || (int64_t)s.B * (s.k + 2) > 0x7fffffffLL) return SV_ERR_SHAPE;
-  if (!(s.temperature >= 0.f) || s.temperature == __builtin_inff()) return SV_ERR_TEMPERATURE;
   const bool greedy = s.temperature == 0.f;
   const int req_layout = aux ? aux->item_layout : SV_LAYOUT_AUTO;
-  if (req_layout != SV_LAYOUT_AUTO && req_layout != SV_LAYOUT_LAUNCH && req_layout != SV_LAYOUT_XCD_RUNS)
-    return SV_ERR_SHAPE;
-  if (s.B == 0) return SV_OK;
-  if (!target_logits || !accepted_len || !out_tokens || !topk_val || !topk_idx) return SV_ERR_NULL;
-  if (s.k > 0 && !draft_tokens) return SV_ERR_NULL;
-  if (!greedy && ((s.k > 0 && !draft_logits) || !uniforms)) return SV_ERR_NULL;
   const Layout L = layout_for(s.B, s.k, s.V, s.dtype);
   if (noalloc) {
     if (L.total > (size_t)SV_NOALLOC_MAX_BYTES) return SV_ERR_SCRATCH;
@@ -1258,7 +1205,8 @@ int verify_impl(const sv_shape_t *shape, const void *target_logits, const void *
     hipLaunchKernelGGL(sv_zero_fill, dim3(g), dim3(256), 0, (hipStream_t)stream, (u32x4 *)workspace, n16);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   }
-  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return SV_ERR_WORKSPACE;
+  const int rc1 = sv_host::check_workspace(L, workspace, workspace_bytes);
+  if (rc1 != SV_OK) return rc1;
 
   char *ws = (char *)workspace;
   Params P;
