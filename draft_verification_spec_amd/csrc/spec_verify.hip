@@ -84,10 +84,11 @@ constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 // B = 1..256, k = 3..8), with fp32 logits nontemporal ones (7 us per step at
 // B = 32, k = 15).
 template <int DT> constexpr bool kStreamNT = DT == SV_F32;
-// Waves per SIMD the kernel is built for: 8 for fp32 (64 VGPRs, a spill of 8
-// bytes only on the merge's rare rescan path; at B = 32, k = 15 greedy 83.6 ->
-// 80.3 us, sampling 135.6 -> 132.6 us); the format's budget for bf16, which
-// at 7 or 8 waves spills on hot paths (greedy at 8: 112 bytes).
+// Waves per SIMD the kernel is built for: 8 for fp32 (64 VGPRs; at B = 32,
+// k = 15 greedy 83.6 -> 80.3 us, sampling 135.6 -> 132.6 us against 6); the
+// format's budget for bf16 (80 VGPRs), which at 7 or 8 waves spills on hot
+// paths.  None of the four builds uses scratch memory; the SGPRs the compiler
+// spills (kernel arguments, mostly) go to VGPR lanes.
 template <int DT, bool GREEDY> constexpr int kWaves = DT == SV_F32 ? 8 : Fmt<DT>::WAVES;
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
 // Published per (group, tile) by the stream workgroups; 8 words.
@@ -382,10 +383,10 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
     zero_recs(P.grec + (int64_t)b * K1, K1);
   } else if (tid == 0) {
     // the draw workgroups read the group records until they finish, and clear them
+    // j and the state go out in one 64-bit store: a reader that sees the
+    // state sees j, with no wait between the two
     SeqRec *rec = (SeqRec *)((char *)P.srec + (int64_t)b * SREC_STRIDE);
-    st_dev(&rec->j, j);
-    stores_done();
-    st_dev(&rec->state, st ? 2 : 1);
+    st_dev((uint64_t *)rec, ((uint64_t)(uint32_t)(st ? 2 : 1) << 32) | (uint32_t)j);
   }
 }
 
@@ -552,6 +553,12 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     seq_finish<DT, GREEDY>(P, b, sm);
   }
 
+  // which slots hold a key (to clear them at the end), so that the keys
+  // themselves are dead across the rescans below
+  uint32_t kheld = 0;
+#pragma unroll
+  for (int q = 0; q < KEYS_PT; ++q) kheld |= key[q] ? 1u << q : 0u;
+
   // ---- candidates at or above the bound: slots of complete tiles, then rescans
   if (!nanrow) {
 #pragma unroll
@@ -609,14 +616,18 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     gr.flags = fl; gr.argmax = sm.bc[6]; gr.accept = 1; gr.ready = 0;
     st_rec(P.grec + g, gr);
   }
-  // the group record is out: announce it, then clear the group's workspace
-  // (nothing in this launch reads it again)
-  block_stores_done();
-  if (GREEDY && i != k && tid == 0) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
+  // greedy: announce the group record once thread 0's stores of it have
+  // completed.  Then clear the group's workspace: nothing in this launch reads
+  // it again, so no wave waits for these stores (waiting for all of the
+  // merge's stores measured ~5 us slower per step at B = 256, k = 3)
+  if (GREEDY && wid == 0) {
+    stores_done();
+    if (i != k && tid == 0) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
+  }
 #pragma unroll
   for (int q = 0; q < KEYS_PT; ++q) {
     const int a = tid + q * TPB;
-    if (a < nslot && key[q]) st_dev(slots + a, (uint64_t)0);
+    if ((kheld >> q) & 1u) st_dev(slots + a, (uint64_t)0);
   }
   if (own) {
     // (sampling: row k's maximum and sum words stay for a bonus draw; the

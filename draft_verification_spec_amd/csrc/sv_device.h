@@ -145,11 +145,6 @@ __device__ __forceinline__ void stores_done() {
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
-// All of the workgroup's stores have completed (every wave waited for its own).
-__device__ __forceinline__ void block_stores_done() {
-  stores_done();
-  __syncthreads();
-}
 // Bounded wait of one thread until *p >= target.  Returns the value seen;
 // on timeout sets fault bit 1 and returns what it last saw.
 __device__ __forceinline__ int wait_at_least(const int32_t *p, int target, int32_t *fault) {
