@@ -569,23 +569,30 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         if (pos < MERGE_CAP) sm.keys[pos] = key[q];
       }
     }
+    // (a rescanned tile is read in two halves of NSEG / 2 vectors per thread,
+    // which keeps this rare path within the streaming path's registers)
+    constexpr int HS = NSEG / 2, HALF = TPB * HS * Fmt<DT>::W;
     uint64_t m = rs;
     while (m) {
       const int tc = __builtin_ctzll(m);
       m &= m - 1;
-      u32x4 r[NSEG];
-      load_tile<DT, false, NSEG, kStreamNT<DT>>(G.trow, tc, V, P.t_vec, r);
-      const int lim = V - tc * Fmt<DT>::TILE;
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        u32x4 r[HS];
+        load_tile<DT, false, HS, kStreamNT<DT>>(G.trow, 2 * tc + h, V, P.t_vec, r);
+        const int x0 = tc * Fmt<DT>::TILE + h * HALF;
 #pragma unroll
-      for (int s = 0; s < NSEG; ++s)
+        for (int s = 0; s < HS; ++s)
 #pragma unroll
-        for (int w = 0; w < Fmt<DT>::W; ++w) {
-          const float xv = unpack<DT>(r[s], w);
-          if (tpos<DT>(s, w) < lim && xv == xv && ordered_key(xv) >= rb) {
-            const int pos = atomicAdd(&sm.bc[0], 1);
-            if (pos < MERGE_CAP) sm.keys[pos] = cand_key(xv, tc * Fmt<DT>::TILE + tpos<DT>(s, w));
+          for (int w = 0; w < Fmt<DT>::W; ++w) {
+            const float xv = unpack<DT>(r[s], w);
+            const int x = x0 + tpos<DT>(s, w);
+            if (x < V && xv == xv && ordered_key(xv) >= rb) {
+              const int pos = atomicAdd(&sm.bc[0], 1);
+              if (pos < MERGE_CAP) sm.keys[pos] = cand_key(xv, x);
+            }
           }
-        }
+      }
     }
   }
   __syncthreads();
@@ -759,6 +766,10 @@ __device__ __forceinline__ void draw_crossing(const Params &P, int b, int c, int
   __syncthreads();
   if (wid == 0) {
     constexpr int NE = NSEG * W;                     // elements per thread (<= 64)
+    // the assembly's state (the token stands unless it found a data error),
+    // read while the walk below runs (by every lane: one request, and no
+    // lane mask that would make the compiler wait for it at once)
+    int state = ld_dev(&rec->state);
     int pos = -1;
     if (walker >= 0) {
       const float m = lane < NE ? mass_of(elem_of_words<DT>(sm.walk.t, lane), elem_of_words<DT>(sm.walk.d, lane),
@@ -776,9 +787,10 @@ __device__ __forceinline__ void draw_crossing(const Params &P, int b, int c, int
       const int e = pass ? __builtin_ctzll(pass) : (posm ? 63 - __builtin_clzll(posm) : -1);
       pos = e < 0 ? -1 : walker * NE + e;
     }
-    // the token stands unless the assembly found a data error
-    if (lane == 0 && wait_at_least(&rec->state, 1, P.fault) == 1)
-      P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+    if (lane == 0) {
+      if (state == 0) state = wait_at_least(&rec->state, 1, P.fault);
+      if (state == 1) P.out_tokens[(int64_t)b * K1 + j] = pos < 0 ? -1 : c * Fmt<DT>::TILE + pos;
+    }
   }
 }
 

@@ -256,13 +256,26 @@ __device__ __forceinline__ void load_tile(const char *row, int c, int V, bool ve
     }
     return;
   }
+  // the row's last tile, or a row without 16-byte alignment.  First every
+  // vector that lies in the row, with no wait between the loads: vectors past
+  // V hold -inf (set before the loads, so that no lane's constant waits for
+  // another lane's load).  Then, element by element, a vector that straddles V
+  // (at most one per row and tile, none when V is a multiple of the vector
+  // width) or every vector of an unaligned row.
+  constexpr uint32_t NEG = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int64_t e0 = c0 + (TM ? dpos<DT>(s, 0) : tpos<DT>(s, 0));
+    r[s] = u32x4{NEG, NEG, NEG, NEG};
     if (vec && e0 + W <= V) {
       if (NT) r[s] = __builtin_nontemporal_load((const u32x4 *)(row + e0 * E));
       else r[s] = *(const u32x4 *)(row + e0 * E);
-    } else {
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int64_t e0 = c0 + (TM ? dpos<DT>(s, 0) : tpos<DT>(s, 0));
+    if (!(vec && e0 + W <= V) && e0 < V) {
       u32x4 v;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
