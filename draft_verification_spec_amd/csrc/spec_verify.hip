@@ -77,6 +77,7 @@ using namespace sv_dev;
 constexpr int LIST = 8;                // lane maxima a tile record keeps
 constexpr int SLOTS = 32;              // candidate slots per tile
 constexpr int MERGE_CAP = 512;         // candidates a row merge ranks in LDS
+constexpr int STAGE = 128;             // candidates a tile stages in LDS (its top SLOTS are published)
 constexpr int TOPK = SV_TOPK;
 constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 // The streaming loads are marked nontemporal for fp32 logits only: with bf16
@@ -1060,7 +1061,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
           for (int w = 0; w < W; ++w) {
             if ((decltype(full)::value || tpos<DT>(s, w) < lim) && et.x[s][w] >= thr) {
               const int slot = atomicAdd(&sm.bc[0], 1);
-              if (slot < SLOTS) sm.keys[slot] = cand_key(et.x[s][w], c * TILE + tpos<DT>(s, w));
+              if (slot < STAGE) sm.keys[slot] = cand_key(et.x[s][w], c * TILE + tpos<DT>(s, w));
             }
           }
         }
@@ -1088,18 +1089,33 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
         s_ct += rescale(sm.d[0][w], sm.f[0][w], m_ct, P.sc);
         s_cd += rescale(sm.d[1][w], sm.f[1][w], m_cd, P.sc);
       }
+    // more candidates than slots, all of them staged: the tile publishes its
+    // own 32 largest (by key, ranked by counting) and a threshold of 0.  Its
+    // other elements each lie below 32 published ones, so none can be among
+    // the row's 32 largest and the merge never rescans the tile.  Beyond the
+    // stage the overflow flag asks for a rescan.
+    const int nc = sm.bc[0];
+    const bool own32 = nc > SLOTS && nc <= STAGE;
     if (lane < 8) {
       uint64_t word;
       if (lane == 0) word = ((uint64_t)__float_as_uint(m_cd) << 32) | __float_as_uint(m_ct);
       else if (lane == 1) word = __builtin_bit_cast(uint64_t, s_ct);
       else if (lane == 2) word = __builtin_bit_cast(uint64_t, s_cd);
-      else if (lane == 3) word = ((uint64_t)kthr << 32) | (uint32_t)(f_ct | (f_cd << 8));
+      else if (lane == 3) word = ((uint64_t)(own32 ? 0u : kthr) << 32) | (uint32_t)(f_ct | (f_cd << 8));
       else word = ((uint64_t)sm.w8[2 * (lane - 4) + 1] << 32) | sm.w8[2 * (lane - 4)];
       st_dev((uint64_t *)(P.recs + item) + lane, word);
     }
-    const int nc = sm.bc[0];
-    if (lane < SLOTS && lane < nc) st_dev(P.cand + (int64_t)item * SLOTS + lane, sm.keys[lane]);
-    if (lane == 0 && nc > SLOTS) st_dev(P.ovf + item, 1);
+    if (!own32) {
+      if (lane < SLOTS && lane < nc) st_dev(P.cand + (int64_t)item * SLOTS + lane, sm.keys[lane]);
+      if (lane == 0 && nc > STAGE) st_dev(P.ovf + item, 1);
+    } else {
+      for (int q = lane; q < nc; q += 64) {
+        const uint64_t kq = sm.keys[q];
+        int rank = 0;
+        for (int jj = 0; jj < nc; ++jj) rank += sm.keys[jj] > kq;
+        if (rank < SLOTS) st_dev(P.cand + (int64_t)item * SLOTS + rank, kq);
+      }
+    }
     stores_done();
   }
   if (c != P.nT - 1) {                                   // not the group's last tile: announce and leave

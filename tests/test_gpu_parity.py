@@ -281,6 +281,67 @@ def test_top32_ties_and_constant_rows(sv, orc):
     np.testing.assert_array_equal(o["topk_val"].view(np.uint32), g["topk_val"].view(np.uint32))
 
 
+def _tile_pos(dtype, c, t, s, w):
+    """Row index of element w of vector s of thread t in tile c, in the
+    streaming layout (thread t owns vectors at s * 256 * W + t * W)."""
+    W = 8 if dtype == sv_inputs.BF16 else 4
+    return c * 1024 * W + s * 256 * W + t * W + w
+
+
+@pytest.mark.parametrize("dtype", [sv_inputs.BF16, sv_inputs.F32])
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_top32_crowded_tiles(sv, orc, dtype, T):
+    """A tile with 57 elements at or above its candidate threshold (it
+    publishes its own 32 largest) and one with over 128 (overflow: the merge
+    rescans it), in rows whose top-32 takes about 22 elements from the first
+    and 10 from the second."""
+    V = 40000
+    B, k = 3, 1
+    W = 8 if dtype == sv_inputs.BF16 else 4
+    w = sv_inputs.make_workload("crowded", B, k, V, dtype, T, 2101, 1.0, 0.5, draft_T=T)
+    rng = np.random.default_rng(7)
+    x = (-4.0 + 0.25 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+
+    def crowd(row, c, lanes, per_lane, vals):
+        # per wave, lanes 0..lanes-1 (wave 3: lane 0 only) hold per_lane of the
+        # values; wave 3's lane 1 holds 0.5, so the tile's threshold (the
+        # smallest of the 8 listed lane maxima) is 0.5
+        it = iter(vals)
+        for wave in range(4):
+            for ln in (range(lanes) if wave < 3 else (0,)):
+                for e in range(per_lane):
+                    row[_tile_pos(dtype, c, wave * 64 + ln, e // W, e % W)] = next(it)
+        row[_tile_pos(dtype, c, 3 * 64 + 1, 0, 0)] = 0.5
+        return row
+
+    for b in range(B):
+        for i in range(k + 1):
+            # tile 0: 7 lanes x 8 values in [14, 28], step 1/4 (exact in bf16)
+            crowd(x[b, i], 0, 2, 8, 14.0 + np.arange(56) / 4.0 + 0.25 * b)
+            # tile 1: over 128 values in [3, 24], step 1/8
+            n1 = 10 * 4 * W if W == 4 else 7 * 24
+            lanes1, per1 = (3, 4 * W) if W == 4 else (2, 24)
+            crowd(x[b, i], 1, lanes1, per1, 3.0 + np.arange(n1) / 8.0)
+    if dtype == sv_inputs.BF16:
+        w.target = sv_inputs.bf16_round(x)
+        w.draft = sv_inputs.bf16_round(x[:, :k] + 0.1)
+    else:
+        w.target = x
+        w.draft = (x[:, :k] + np.float32(0.1)).astype(np.float32)
+    o, g = orc.verify_workload(w), run_gpu(sv, w)
+    for key in ("topk_idx", "status"):
+        np.testing.assert_array_equal(o[key], g[key], err_msg=key)
+    np.testing.assert_array_equal(o["topk_val"].view(np.uint32), g["topk_val"].view(np.uint32))
+    # both tiles contribute to every row's top-32
+    tile_of_idx = o["topk_idx"] // (1024 * W)
+    assert ((tile_of_idx == 0).sum(axis=-1) > 0).all() and ((tile_of_idx == 1).sum(axis=-1) > 0).all()
+    if T == 0:
+        for key in ("accepted_len", "out_tokens"):
+            np.testing.assert_array_equal(o[key], g[key], err_msg=key)
+    else:
+        check_parity(o, g, w)
+
+
 def test_data_errors(sv, orc):
     V = 5000
     w = sv_inputs.make_workload("errors", 8, 2, V, sv_inputs.F32, 1.0, 1901, 2.0, 0.5)
