@@ -8,6 +8,7 @@ verify needs the built library and an MI355X, and raises if either is missing.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 import re
@@ -140,6 +141,16 @@ def spec_verify_noalloc(shape: Optional[sv_shape_t], target_logits, draft_logits
 Result = namedtuple("Result", "accepted_len out_tokens topk_val topk_idx status lse_target lse_draft p_tok q_tok")
 
 _workspaces = {}
+
+
+def _release_workspaces():
+    """At interpreter exit, before native tear-down (a profiler's or the HIP
+    runtime's own exit handlers run after Python's): drop the cached
+    workspaces, so that no device buffer of this module outlives them."""
+    _workspaces.clear()
+
+
+atexit.register(_release_workspaces)
 
 
 def workspace_for(device, nbytes: int):
