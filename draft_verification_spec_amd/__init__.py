@@ -38,10 +38,12 @@ class sv_shape_t(ctypes.Structure):
 
 class sv_aux_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_void_p), ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p),
-                ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p), ("item_layout", ctypes.c_int32)]
+                ("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p), ("item_layout", ctypes.c_int32),
+                ("variant", ctypes.c_int32)]
 
 
 SV_LAYOUT_AUTO, SV_LAYOUT_LAUNCH, SV_LAYOUT_XCD_RUNS = 0, 1, 2
+SV_VARIANT_AUTO, SV_VARIANT_BASE, SV_VARIANT_HIGH_OCC = 0, 1, 2
 
 
 class sv_kd_shape_t(ctypes.Structure):
@@ -74,6 +76,8 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_workspace_bytes.restype = ctypes.c_size_t
         lib.spec_verify_layout_choice.argtypes = [ctypes.POINTER(sv_shape_t)]
         lib.spec_verify_layout_choice.restype = ctypes.c_int
+        lib.spec_verify_variant_choice.argtypes = [ctypes.POINTER(sv_shape_t)]
+        lib.spec_verify_variant_choice.restype = ctypes.c_int
         lib.spec_verify_error_string.argtypes = [ctypes.c_int]
         lib.spec_verify_error_string.restype = ctypes.c_char_p
         lib.spec_verify.argtypes = [ctypes.POINTER(sv_shape_t), P, P, P, P, P, P, P, P,
@@ -110,6 +114,10 @@ def spec_verify_workspace_bytes(shape: sv_shape_t) -> int:
 
 def spec_verify_layout_choice(shape: sv_shape_t) -> int:
     return int(load_library().spec_verify_layout_choice(ctypes.byref(shape)))
+
+
+def spec_verify_variant_choice(shape: sv_shape_t) -> int:
+    return int(load_library().spec_verify_variant_choice(ctypes.byref(shape)))
 
 
 def spec_verify_error_string(code: int) -> str:
@@ -193,7 +201,8 @@ def _row_stride(t, rows_per_seq):
 
 
 def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bool = False,
-           workspace=None, stream=None, events=None, layout: int = SV_LAYOUT_AUTO) -> Result:
+           workspace=None, stream=None, events=None, layout: int = SV_LAYOUT_AUTO,
+           variant: int = SV_VARIANT_AUTO) -> Result:
     """Verify on torch tensors of one device.
 
     target [B,k+1,V] and draft [B,k,V] (float32 or bfloat16, same dtype; draft
@@ -201,8 +210,8 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bo
     [B,k+2] float32 (None allowed when temperature == 0).  events: optional
     pair of torch.cuda.Event recorded on the current stream right before and
     after the call (the launch must then be on the current stream).  layout:
-    SV_LAYOUT_* order of the streaming items (results do not depend on it).
-    Returns device tensors.
+    SV_LAYOUT_* order of the streaming items, variant: SV_VARIANT_* kernel build
+    (results depend on neither).  Returns device tensors.
     """
     import torch
     if target.dim() != 3:
@@ -247,14 +256,15 @@ def verify(target, draft, draft_tokens, uniforms, temperature: float, *, aux: bo
     tv = torch.empty(B, K1, TOPK, **f32)
     ti = torch.empty(B, K1, TOPK, **i32)
     st = torch.empty(B, **i32)
-    a = sv_aux_t(st.data_ptr(), None, None, None, None, int(layout))
+    a = sv_aux_t(st.data_ptr(), None, None, None, None, int(layout), int(variant))
     lt = ld = pt = qt = None
     if aux and not greedy:
         lt = torch.empty(B, K1, **f32)
         ld = torch.empty(B, k, **f32)
         pt = torch.empty(B, k, **f32)
         qt = torch.empty(B, k, **f32)
-        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr(), int(layout))
+        a = sv_aux_t(st.data_ptr(), lt.data_ptr(), ld.data_ptr(), pt.data_ptr(), qt.data_ptr(), int(layout),
+                     int(variant))
     nbytes = spec_verify_workspace_bytes(shape)
     ws = workspace if workspace is not None else workspace_for(dev, nbytes)
     cur = torch.cuda.current_stream(dev)

@@ -86,11 +86,14 @@ constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 // B = 32, k = 15).
 template <int DT> constexpr bool kStreamNT = DT == SV_F32;
 // Waves per SIMD the kernel is built for: 8 for fp32 (64 VGPRs; at B = 32,
-// k = 15 greedy 83.6 -> 80.3 us, sampling 135.6 -> 132.6 us against 6); the
-// format's budget for bf16 (80 VGPRs), which at 7 or 8 waves spills on hot
-// paths.  None of the four builds uses scratch memory; the SGPRs the compiler
+// k = 15 greedy 83.6 -> 80.3 us, sampling 135.6 -> 132.6 us against 6).  bf16
+// has two builds, chosen per shape by the measured table: the format's budget
+// (6 waves, 80 VGPRs) and a high-occupancy one (7 waves in sampling, 8 in
+// greedy), which keeps more workgroups resident at large batches but measured
+// slower at small ones.  No build uses scratch memory; the SGPRs the compiler
 // spills (kernel arguments, mostly) go to VGPR lanes.
-template <int DT, bool GREEDY> constexpr int kWaves = DT == SV_F32 ? 8 : Fmt<DT>::WAVES;
+template <int DT, bool GREEDY, bool HI> constexpr int kWaves =
+    DT == SV_F32 ? 8 : (HI ? (GREEDY ? 8 : 7) : Fmt<DT>::WAVES);
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
 // Published per (group, tile) by the stream workgroups; 8 words.
 struct TileRec {
@@ -815,7 +818,7 @@ __device__ __forceinline__ void draw_crossing(const Params &P, int b, int c, int
 // crossing that rounding moves past the tile's end).  A sequence's draw workgroups are consecutive, so each waits
 // only for workgroups dispatched with it or before it.  The last one to finish
 // clears the sequence's state.
-template <int DT>
+template <int DT, bool HI>
 __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &sm) {
   constexpr int W = Fmt<DT>::W;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -901,7 +904,9 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
   } else if (j >= 0) {
     const bool resid = true;           // j < k: the residual of pair row j
     const float ot = sm.f[2][0], od = sm.f[2][1];
-    const double u = sm.dbc[2];
+    // (the high-occupancy build reads the uniform where it is used, one value
+    // fewer held across the masses)
+    const double u = HI ? 0.0 : sm.dbc[2];
     const char *trow = P.target + ((int64_t)b * K1 + j) * P.tstride * Fmt<DT>::E;
     const char *drow = resid ? P.draft + ((int64_t)b * k + j) * P.dstride * Fmt<DT>::E : nullptr;
     u32x4 rt[NSEG], rd[NSEG];
@@ -946,7 +951,7 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
         }
         const double cum = wave_scan_d(lane < nT ? tot_value(tw) : 0.0);
         const double R = readlane_d(cum, 63);
-        const double tau = u * R;
+        const double tau = (HI ? sm.dbc[2] : u) * R;
         const uint64_t h = __ballot(lane < nT && cum > tau);
         const int cs = h ? __builtin_ctzll(h) : nT - 1;
         const double before = cs > 0 ? readlane_d(cum, cs - 1) : 0.0;
@@ -977,15 +982,17 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
   if (tid == 0) st_dev(P.ddone + (int64_t)b * CTR, 0);
 }
 
-template <int DT, bool GREEDY>
-__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, GREEDY>, 8))) void sv_verify(Params P) {
+template <int DT, bool GREEDY, bool HI>
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, GREEDY, HI>, 8))) void sv_verify(Params P) {
   __shared__ Smem sm;
   constexpr int W = Fmt<DT>::W, TILE = Fmt<DT>::TILE;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int V = P.V;
   if (!GREEDY && (int)blockIdx.x >= P.items) {           // draw workgroups come last
     const int d = blockIdx.x - P.items;
-    draw_tile<DT>(P, d / P.nT, d - (d / P.nT) * P.nT, sm);
+    int b = d / P.nT;
+    if constexpr (HI) b = __builtin_amdgcn_readfirstlane(b);   // kept in a scalar register
+    draw_tile<DT, HI>(P, b, d - b * P.nT, sm);
     return;
   }
   const int item = P.xcd_runs ? xcd_item(blockIdx.x, P.items) : (int)blockIdx.x;
@@ -1137,6 +1144,7 @@ using sv_host::Layout;
 using sv_host::layout_for;
 using sv_host::shape_ok;
 using sv_host::table_layout;
+using sv_host::table_variant;
 using sv_host::tile_of;
 static_assert(sizeof(TileRec) == sv_host::TILE_REC_BYTES && sizeof(GroupRec) == sv_host::GROUP_REC_BYTES &&
                   SREC_STRIDE == (int)sv_host::SEQ_REC_BYTES && SLOTS == sv_host::SLOTS && CTR == sv_host::CTR &&
@@ -1144,11 +1152,19 @@ static_assert(sizeof(TileRec) == sv_host::TILE_REC_BYTES && sizeof(GroupRec) == 
               "host layout constants");
 
 template <int DT>
-hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
-  // streaming workgroups, then (sampling) one draw workgroup per (sequence, tile)
+hipError_t launch(const Params &P, bool greedy, bool hi, hipStream_t stream) {
+  // streaming workgroups, then (sampling) one draw workgroup per (sequence, tile);
+  // fp32 has one build
   const unsigned grid = (unsigned)P.items + (greedy ? 0u : (unsigned)P.B * (unsigned)P.nT);
-  if (greedy) hipLaunchKernelGGL((sv_verify<DT, true>), dim3(grid), dim3(TPB), 0, stream, P);
-  else hipLaunchKernelGGL((sv_verify<DT, false>), dim3(grid), dim3(TPB), 0, stream, P);
+  if constexpr (DT == SV_BF16) {
+    if (hi) {
+      if (greedy) hipLaunchKernelGGL((sv_verify<DT, true, true>), dim3(grid), dim3(TPB), 0, stream, P);
+      else hipLaunchKernelGGL((sv_verify<DT, false, true>), dim3(grid), dim3(TPB), 0, stream, P);
+      return hipGetLastError();
+    }
+  }
+  if (greedy) hipLaunchKernelGGL((sv_verify<DT, true, false>), dim3(grid), dim3(TPB), 0, stream, P);
+  else hipLaunchKernelGGL((sv_verify<DT, false, false>), dim3(grid), dim3(TPB), 0, stream, P);
   return hipGetLastError();
 }
 
@@ -1157,6 +1173,11 @@ hipError_t launch(const Params &P, bool greedy, hipStream_t stream) {
 extern "C" int spec_verify_layout_choice(const sv_shape_t *s) {
   if (!s || !shape_ok(s) || !(s->temperature >= 0.f) || s->temperature == __builtin_inff()) return 0;
   return table_layout(s);
+}
+
+extern "C" int spec_verify_variant_choice(const sv_shape_t *s) {
+  if (!s || !shape_ok(s) || !(s->temperature >= 0.f) || s->temperature == __builtin_inff()) return 0;
+  return table_variant(s);
 }
 
 extern "C" size_t spec_verify_workspace_bytes(const sv_shape_t *s) {
@@ -1232,6 +1253,7 @@ int verify_impl(const sv_shape_t *shape, const void *target_logits, const void *
   const int64_t items = (int64_t)s.B * (s.k + 1) * nT;
   const bool greedy = s.temperature == 0.f;
   const int req_layout = aux ? aux->item_layout : SV_LAYOUT_AUTO;
+  const int req_variant = aux ? aux->variant : SV_VARIANT_AUTO;
   const Layout L = layout_for(s.B, s.k, s.V, s.dtype);
   if (noalloc) {
     if (L.total > (size_t)SV_NOALLOC_MAX_BYTES) return SV_ERR_SCRATCH;
@@ -1287,8 +1309,9 @@ int verify_impl(const sv_shape_t *shape, const void *target_logits, const void *
   P.t_vec = (((uintptr_t)target_logits & 15) == 0 && ((ts * esz) & 15) == 0) ? 1 : 0;
   P.d_vec = (!greedy && s.k > 0 && ((uintptr_t)draft_logits & 15) == 0 && ((ds * esz) & 15) == 0) ? 1 : 0;
 
-  const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, (hipStream_t)stream)
-                                          : launch<SV_F32>(P, greedy, (hipStream_t)stream);
+  const bool hi = (req_variant == SV_VARIANT_AUTO ? table_variant(&s) : req_variant) == SV_VARIANT_HIGH_OCC;
+  const hipError_t e = s.dtype == SV_BF16 ? launch<SV_BF16>(P, greedy, hi, (hipStream_t)stream)
+                                          : launch<SV_F32>(P, greedy, hi, (hipStream_t)stream);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -57,6 +57,22 @@ inline bool shape_ok(const sv_shape_t *s) {
          (int64_t)s->V <= (int64_t)MAX_TILES * tile_of(s->dtype);
 }
 
+// The table entry nearest to a shape in (log2 B, log2(k + 1)) among those of
+// its dtype and mode; nullptr when there is none.
+inline const SvLayoutEntry *table_entry(const sv_shape_t *s) {
+  const bool greedy = s->temperature == 0.f;
+  double best = 1e30;
+  const SvLayoutEntry *hit = nullptr;
+  for (const SvLayoutEntry *e = kSvLayoutTable; e->dtype >= 0; ++e) {
+    if (e->dtype != s->dtype || e->greedy != (greedy ? 1 : 0)) continue;
+    const double db = log2((double)(s->B > 0 ? s->B : 1)) - log2((double)e->B);
+    const double dk = log2((double)s->k + 1.0) - log2((double)e->k + 1.0);
+    const double d = db * db + dk * dk;
+    if (d < best) { best = d; hit = e; }
+  }
+  return hit;
+}
+
 // The item layout for a shape.  In launch order, tile c of every group goes
 // to XCD (g * nT + c) mod 8, so with a tile count divisible by 4 the groups'
 // last tiles, which run the merges, crowd onto 2 or 1 of the 8 XCDs (a 16-tile
@@ -66,17 +82,15 @@ inline bool shape_ok(const sv_shape_t *s) {
 inline int table_layout(const sv_shape_t *s) {
   const int nT = (s->V + tile_of(s->dtype) - 1) / tile_of(s->dtype);
   if (nT % 4 == 0) return SV_LAYOUT_XCD_RUNS;
-  const bool greedy = s->temperature == 0.f;
-  double best = 1e30;
-  int layout = SV_LAYOUT_XCD_RUNS;
-  for (const SvLayoutEntry *e = kSvLayoutTable; e->dtype >= 0; ++e) {
-    if (e->dtype != s->dtype || e->greedy != (greedy ? 1 : 0)) continue;
-    const double db = log2((double)(s->B > 0 ? s->B : 1)) - log2((double)e->B);
-    const double dk = log2((double)s->k + 1.0) - log2((double)e->k + 1.0);
-    const double d = db * db + dk * dk;
-    if (d < best) { best = d; layout = e->layout; }
-  }
-  return layout;
+  const SvLayoutEntry *e = table_entry(s);
+  return e ? e->layout : SV_LAYOUT_XCD_RUNS;
+}
+
+// The kernel build for a shape: the nearest table entry's (bf16; fp32 has one).
+inline int table_variant(const sv_shape_t *s) {
+  if (s->dtype != SV_BF16) return SV_VARIANT_BASE;
+  const SvLayoutEntry *e = table_entry(s);
+  return e ? e->variant : SV_VARIANT_BASE;
 }
 
 // Every host-detectable argument check of spec_verify except the workspace,
@@ -102,6 +116,9 @@ inline int check_args(const sv_shape_t *shape, const void *target_logits, const 
   const bool greedy = s.temperature == 0.f;
   const int req_layout = aux ? aux->item_layout : SV_LAYOUT_AUTO;
   if (req_layout != SV_LAYOUT_AUTO && req_layout != SV_LAYOUT_LAUNCH && req_layout != SV_LAYOUT_XCD_RUNS)
+    return SV_ERR_SHAPE;
+  const int req_variant = aux ? aux->variant : SV_VARIANT_AUTO;
+  if (req_variant != SV_VARIANT_AUTO && req_variant != SV_VARIANT_BASE && req_variant != SV_VARIANT_HIGH_OCC)
     return SV_ERR_SHAPE;
   if (s.B == 0) {
     *nothing = true;

@@ -1,18 +1,21 @@
-"""Measure the verification kernel's two item layouts over batch sizes and
-draft lengths on the GPU, and write the table the library's SV_LAYOUT_AUTO
-uses (csrc/sv_dispatch.h) with a summary (profiles/dispatch_layout_V151936.md).
+"""Measure the verification kernel's two item layouts and, for bf16 logits, its
+two builds (6 waves per SIMD, or 7 in sampling and 8 in greedy) over batch
+sizes and draft lengths on the GPU, and write the table the library's
+SV_LAYOUT_AUTO and SV_VARIANT_AUTO use (csrc/sv_dispatch.h) with a summary
+(profiles/dispatch_layout_V151936.md).
 
     python -m draft_verification_spec_amd.dispatch_table     # on an MI355X; rebuild afterwards
 
 Inputs are timing inputs only, generated on the device (seeded): target logits
 N(0, 3^2), draft = target + N(0, 1), drafted tokens drawn from the draft
 softmax by the Gumbel-max trick, uniforms U[0, 1).  Timing is on the device:
-for each layout one HIP graph holds one call per input copy (the copies rotate,
-up to 1 GB, so logits come from HBM); HIP events on the stream bracket a number
-of replays, so the host's per-call cost stays out.  The two layouts alternate
-five times per configuration; the table keeps the layout with the lower best
-time per call.  The layouts give identical results; only the order in which
-streaming workgroups take the (group, tile) items differs.
+for each (layout, build) one HIP graph holds one call per input copy (the
+copies rotate, up to 1 GB, so logits come from HBM); HIP events on the stream
+bracket a number of replays, so the host's per-call cost stays out.  The
+combinations alternate five times per configuration; the table keeps the one
+with the lower best time per call.  They give identical results; only the order
+in which streaming workgroups take the (group, tile) items, and how many
+workgroups are resident at once, differ.
 """
 import os
 import sys
@@ -52,8 +55,9 @@ def measure(torch, sv, dt, greedy, B, k, calls=48, rounds=5):
     tv = torch.empty(B, k + 1, sv.TOPK, dtype=torch.float32, device=dev)
     ti = torch.empty(B, k + 1, sv.TOPK, **i32)
     graphs = {}
-    for layout in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS):
-        aux = sv.sv_aux_t(st.data_ptr(), None, None, None, None, layout)
+    variants = (sv.SV_VARIANT_BASE, sv.SV_VARIANT_HIGH_OCC) if dt == "bf16" else (sv.SV_VARIANT_BASE,)
+    for combo in [(lay, var) for var in variants for lay in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS)]:
+        aux = sv.sv_aux_t(st.data_ptr(), None, None, None, None, combo[0], combo[1])
 
         def call(i, stream, aux=aux):
             a, b = sets[i % copies]
@@ -71,12 +75,12 @@ def measure(torch, sv, dt, greedy, B, k, calls=48, rounds=5):
             for i in range(copies):
                 call(i, cs)
         torch.cuda.synchronize()
-        graphs[layout] = g
+        graphs[combo] = g
     reps = max(1, calls // copies)
     best = {}
     stream = torch.cuda.current_stream()
     for rnd in range(rounds):
-        for layout, g in graphs.items():
+        for combo, g in graphs.items():
             g.replay()                                  # warm
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -85,7 +89,7 @@ def measure(torch, sv, dt, greedy, B, k, calls=48, rounds=5):
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-            best[layout] = min(best.get(layout, 1e30), us)
+            best[combo] = min(best.get(combo, 1e30), us)
     del graphs, sets, t, d
     torch.cuda.empty_cache()
     return best
@@ -95,38 +99,45 @@ def main():
     import torch
     sys.path.insert(0, ROOT)
     import draft_verification_spec_amd as sv
+    L, X = sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS
+    BASE, HIGH = sv.SV_VARIANT_BASE, sv.SV_VARIANT_HIGH_OCC
     rows = []
     for dt, greedy, B, k in GRID:
         best = measure(torch, sv, dt, greedy, B, k)
-        lay = min(best, key=best.get)
-        rows.append((dt, greedy, B, k, best[sv.SV_LAYOUT_LAUNCH], best[sv.SV_LAYOUT_XCD_RUNS], lay))
-        print(f"[dispatch] {dt} {'greedy' if greedy else 'sampling'} B={B} k={k}: launch "
-              f"{best[sv.SV_LAYOUT_LAUNCH]:.2f} us, xcd runs {best[sv.SV_LAYOUT_XCD_RUNS]:.2f} us", flush=True)
-    entries = ",\n".join(f"    {{{B}, {k}, {1 if dt == 'bf16' else 0}, {1 if greedy else 0}, {lay}}}"
-                         for dt, greedy, B, k, _, _, lay in rows)
-    header = f'''// sv_dispatch.h -- item layout per shape for the verification kernel, measured
-// on MI355X by draft_verification_spec_amd/dispatch_table.py (V = {V}): for
-// each (B, k, dtype, mode) the faster of launch order (1) and one run of items
-// per XCD (2).  Timings: profiles/dispatch_layout_V{V}.md.
+        lay, var = min(best, key=best.get)
+        rows.append((dt, greedy, B, k, best, lay, var))
+        print(f"[dispatch] {dt} {'greedy' if greedy else 'sampling'} B={B} k={k}: "
+              + ", ".join(f"{'launch' if c[0] == L else 'xcd'}/{'base' if c[1] == BASE else 'high'} {v:.2f} us"
+                          for c, v in best.items()), flush=True)
+    entries = ",\n".join(f"    {{{B}, {k}, {1 if dt == 'bf16' else 0}, {1 if greedy else 0}, {lay}, {var}}}"
+                         for dt, greedy, B, k, _, lay, var in rows)
+    header = f'''// sv_dispatch.h -- item layout and kernel build per shape for the verification
+// kernel, measured on MI355X by draft_verification_spec_amd/dispatch_table.py
+// (V = {V}): for each (B, k, dtype, mode) the fastest of launch order (1) or
+// one run of items per XCD (2), with the base build (1) or, for bf16, the
+// high-occupancy one (2).  Timings: profiles/dispatch_layout_V{V}.md.
 #pragma once
 #include <stdint.h>
 
 struct SvLayoutEntry {{
-  int32_t B, k, dtype, greedy, layout;
+  int32_t B, k, dtype, greedy, layout, variant;
 }};
 static const SvLayoutEntry kSvLayoutTable[] = {{
 {entries},
-    {{0, 0, -1, -1, 0}},  // (end marker)
+    {{0, 0, -1, -1, 0, 0}},  // (end marker)
 }};
 '''
     out_dir = os.environ.get("SV_DISPATCH_OUT", os.path.join(ROOT, "gpurun_out"))
     os.makedirs(out_dir, exist_ok=True)
     open(os.path.join(out_dir, "sv_dispatch.h"), "w").write(header)
-    lines = ["| dtype | mode | B | k | launch order (us/step) | XCD runs (us/step) | table |",
-             "|---|---|---|---|---|---|---|"]
-    for dt, greedy, B, k, a, b, lay in rows:
-        lines.append(f"| {dt} | {'greedy' if greedy else 'sampling'} | {B} | {k} | {a:.2f} | {b:.2f} | "
-                     f"{'launch' if lay == sv.SV_LAYOUT_LAUNCH else 'xcd runs'} |")
+    fmt = lambda v: f"{v:.2f}" if v is not None else "-"
+    lines = ["| dtype | mode | B | k | launch, base (us/step) | XCD runs, base | launch, high occupancy | "
+             "XCD runs, high occupancy | table |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for dt, greedy, B, k, best, lay, var in rows:
+        lines.append(f"| {dt} | {'greedy' if greedy else 'sampling'} | {B} | {k} | {fmt(best.get((L, BASE)))} | "
+                     f"{fmt(best.get((X, BASE)))} | {fmt(best.get((L, HIGH)))} | {fmt(best.get((X, HIGH)))} | "
+                     f"{'launch' if lay == L else 'xcd runs'}, {'base' if var == BASE else 'high'} |")
     open(os.path.join(out_dir, f"dispatch_layout_V{V}.md"), "w").write("\n".join(lines) + "\n")
     print(f"[dispatch] wrote {out_dir}/sv_dispatch.h and dispatch_layout_V{V}.md", flush=True)
 

@@ -53,7 +53,7 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
 #define SV_ERR_NULL (-1)        /* a required pointer is NULL */
 #define SV_ERR_SHAPE (-2)       /* B < 0, k < 0, V < 1, V above the maximum (524288 for bf16,
                                    262144 for fp32), a row stride < V, sizes too large, or an
-                                   unknown aux->item_layout */
+                                   unknown aux->item_layout or aux->variant */
 #define SV_ERR_TEMPERATURE (-3) /* temperature < 0, NaN or infinite */
 #define SV_ERR_DTYPE (-4)       /* dtype not SV_F32 / SV_BF16 */
 #define SV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than spec_verify_workspace_bytes */
@@ -93,11 +93,20 @@ typedef struct {
                             items: SV_LAYOUT_AUTO (0, the library's measured table),
                             SV_LAYOUT_LAUNCH (launch order) or SV_LAYOUT_XCD_RUNS (one
                             contiguous run of items per XCD); results are identical */
+    int32_t variant;     /* build of the kernel: SV_VARIANT_AUTO (0, the library's measured
+                            table), SV_VARIANT_BASE (bf16 at 6 waves per SIMD) or
+                            SV_VARIANT_HIGH_OCC (bf16 sampling at 7 waves per SIMD, bf16
+                            greedy at 8; fp32 has one build, taken for both); results are
+                            identical */
 } sv_aux_t;
 
 #define SV_LAYOUT_AUTO 0
 #define SV_LAYOUT_LAUNCH 1
 #define SV_LAYOUT_XCD_RUNS 2
+
+#define SV_VARIANT_AUTO 0
+#define SV_VARIANT_BASE 1
+#define SV_VARIANT_HIGH_OCC 2
 
 /* Bytes of device workspace one call with this shape needs. */
 size_t spec_verify_workspace_bytes(const sv_shape_t *shape);
@@ -110,6 +119,14 @@ size_t spec_verify_workspace_bytes(const sv_shape_t *shape);
  * 1..256, draft lengths 0..15, both dtypes and both modes (the entry nearest
  * in log B and k).  Returns 0 for an invalid shape. */
 int spec_verify_layout_choice(const sv_shape_t *shape);
+
+/* The kernel build (SV_VARIANT_BASE or SV_VARIANT_HIGH_OCC) that
+ * SV_VARIANT_AUTO takes for this shape: for bf16 logits the faster one in the
+ * same measured table (the entry nearest in log B and k); a build with more
+ * waves per SIMD keeps more workgroups resident, which pays at large batches
+ * and costs at small ones.  SV_VARIANT_BASE for fp32.  Returns 0 for an invalid
+ * shape. */
+int spec_verify_variant_choice(const sv_shape_t *shape);
 
 /*
  * Enqueue one verification step on `stream` (a hipStream_t; NULL = default

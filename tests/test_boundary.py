@@ -17,7 +17,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = sv.declared_functions()
     assert set(names) == {"spec_verify", "spec_verify_workspace_bytes", "spec_verify_error_string",
-                          "spec_verify_layout_choice", "spec_verify_noalloc", "sv_kd", "sv_kd_workspace_bytes"}
+                          "spec_verify_layout_choice", "spec_verify_variant_choice", "spec_verify_noalloc", "sv_kd",
+                          "sv_kd_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -66,6 +67,19 @@ def test_layout_choice():
     assert f(sv.make_shape(2, 3, 1000, 0, -1.0)) == 0
     bad = sv.sv_aux_t(None, None, None, None, None, 3)
     assert _call(sv.make_shape(2, 3, 1000, 0, 1.0), aux=bad) == sv.SV_ERR_SHAPE
+
+
+def test_variant_choice():
+    f = sv.spec_verify_variant_choice
+    for B in (1, 4, 32, 256):
+        for k in (0, 3, 15):
+            for T in (0.0, 1.0):
+                assert f(sv.make_shape(B, k, 151936, sv.SV_BF16, T)) in (sv.SV_VARIANT_BASE, sv.SV_VARIANT_HIGH_OCC)
+                assert f(sv.make_shape(B, k, 151936, sv.SV_F32, T)) == sv.SV_VARIANT_BASE   # one fp32 build
+    assert f(sv.make_shape(-1, 3, 1000, 1, 1.0)) == 0
+    for v in (-1, 3):
+        bad = sv.sv_aux_t(None, None, None, None, None, sv.SV_LAYOUT_AUTO, v)
+        assert _call(sv.make_shape(2, 3, 1000, 1, 1.0), aux=bad) == sv.SV_ERR_SHAPE
 
 
 def test_host_validation_codes():
@@ -150,23 +164,30 @@ def test_product_path_never_touches_the_oracle():
 
 
 def test_dispatch_table_matches_its_measurement():
-    """The layout table compiled into the library is the one its committed
-    measurement chose: every row of the timing table (the faster layout per
-    dtype, mode, B, k) has the same entry in sv_dispatch.h, in the same order."""
+    """The table compiled into the library is the one its committed measurement
+    chose: every row of the timing table (the fastest item layout and, for
+    bf16, kernel build per dtype, mode, B, k) has the same entry in
+    sv_dispatch.h, in the same order."""
     import re
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     hdr = open(os.path.join(root, "draft_verification_spec_amd", "csrc", "sv_dispatch.h")).read()
     entries = [tuple(int(v) for v in m) for m in
-               re.findall(r"\{(-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+)\}", hdr)]
-    assert entries[-1] == (0, 0, -1, -1, 0)                    # end marker
+               re.findall(r"\{(-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+)\}", hdr)]
+    assert entries[-1] == (0, 0, -1, -1, 0, 0)                 # end marker
+    L, X = sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS
+    B_, H_ = sv.SV_VARIANT_BASE, sv.SV_VARIANT_HIGH_OCC
     rows = []
     for line in open(os.path.join(root, "profiles", "dispatch_layout_V151936.md")):
         p = [x.strip() for x in line.strip().strip("|").split("|")]
-        if len(p) != 7 or p[0] not in ("bf16", "f32"):
+        if len(p) != 9 or p[0] not in ("bf16", "f32"):
             continue
-        launch, xcd = float(p[4]), float(p[5])
-        lay = sv.SV_LAYOUT_LAUNCH if p[6] == "launch" else sv.SV_LAYOUT_XCD_RUNS
-        # the faster of the two (the timings are printed to 0.01 us: equal ones are a tie)
-        assert (launch <= xcd) if lay == sv.SV_LAYOUT_LAUNCH else (xcd <= launch), line
-        rows.append((int(p[2]), int(p[3]), 1 if p[0] == "bf16" else 0, 1 if p[1] == "greedy" else 0, lay))
+        times = {(L, B_): p[4], (X, B_): p[5], (L, H_): p[6], (X, H_): p[7]}
+        times = {c: float(v) for c, v in times.items() if v != "-"}
+        if p[0] == "f32":
+            assert set(times) == {(L, B_), (X, B_)}, line   # fp32 has one build
+        lay_s, var_s = [x.strip() for x in p[8].split(",")]
+        combo = (L if lay_s == "launch" else X, B_ if var_s == "base" else H_)
+        # the fastest (the timings are printed to 0.01 us: equal ones are a tie)
+        assert times[combo] <= min(times.values()), line
+        rows.append((int(p[2]), int(p[3]), 1 if p[0] == "bf16" else 0, 1 if p[1] == "greedy" else 0) + combo)
     assert rows and rows == entries[:-1]

@@ -207,14 +207,19 @@ def test_bonus_draw_tile_edges(sv, orc, dtype):
 
 @pytest.mark.parametrize("which", ["steady", "greedy"])
 def test_layouts_give_identical_results(sv, which):
-    """The two item layouts only reorder which workgroup takes which item."""
+    """The two item layouts only reorder which workgroup takes which item, and
+    the two bf16 builds only differ in how many workgroups are resident: every
+    combination gives the same bits."""
     w = sv_inputs.make_workload("lay", 6, 3, 40000, sv_inputs.BF16, 0.0 if which == "greedy" else 1.0, 1801, 3.0, 1.0)
     t, d, x, u = sv.to_device(w)
     greedy = w.temperature == 0
     res = []
-    for layout in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS, sv.SV_LAYOUT_AUTO):
-        log(f"spec_verify layouts {which} layout={layout}")
-        r = sv.verify(t, None if greedy else d, x, None if greedy else u, w.temperature, aux=not greedy, layout=layout)
+    combos = [(lay, var) for lay in (sv.SV_LAYOUT_LAUNCH, sv.SV_LAYOUT_XCD_RUNS, sv.SV_LAYOUT_AUTO)
+              for var in (sv.SV_VARIANT_BASE, sv.SV_VARIANT_HIGH_OCC, sv.SV_VARIANT_AUTO)]
+    for layout, variant in combos:
+        log(f"spec_verify layouts {which} layout={layout} variant={variant}")
+        r = sv.verify(t, None if greedy else d, x, None if greedy else u, w.temperature, aux=not greedy,
+                      layout=layout, variant=variant)
         torch.cuda.synchronize()
         res.append(gpu_to_numpy(r))
     for other in res[1:]:
