@@ -184,6 +184,13 @@ __device__ __forceinline__ uint64_t cand_key(float v, int32_t x) {
   const uint32_t neg0 = __float_as_uint(v) == 0x80000000u ? 1u : 0u;
   return ((uint64_t)ordered_key(v) << 32) | ((uint64_t)(0xfffffu - (uint32_t)x) << 1) | neg0;
 }
+// A staged candidate before its key is formed: value bits and tile position.
+__device__ __forceinline__ uint64_t raw_cand(float v, int pos) {
+  return ((uint64_t)__float_as_uint(v) << 32) | (uint32_t)pos;
+}
+__device__ __forceinline__ uint64_t key_of_raw(uint64_t r, int x0) {
+  return cand_key(__uint_as_float((uint32_t)(r >> 32)), x0 + (int)(uint32_t)r);
+}
 __device__ __forceinline__ int32_t cand_index(uint64_t k) { return (int32_t)(0xfffffu - ((uint32_t)k >> 1)); }
 __device__ __forceinline__ float cand_value(uint64_t k) {
   return (k & 1u) ? -0.0f : key_value((uint32_t)(k >> 32));
@@ -1055,20 +1062,30 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
 
   // candidates: elements at or above the threshold, gathered in LDS position
   // by position (a position that holds none in any lane costs one compare;
-  // the slot reservation is one LDS atomic per wave and position)
+  // the slot reservation is one LDS atomic per wave and position) as raw
+  // value bits and tile position; wave 0 forms the ordered keys of those it
+  // publishes
   {
     const float thr = key_value(kthr);
     const int lim = V - c * TILE;                        // tile positions < lim exist
     const bool act = has_elem && tkey >= kthr;           // lanes that may hold candidates
+    // (the greedy high-occupancy build, at 64 registers, unpacks the walked
+    // vectors again: its packed elements pass through an empty asm so that
+    // the unpacked copy is not kept live from the statistics)
+    constexpr bool REUNPACK = GREEDY && HI;
+    if (REUNPACK)
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) asm volatile("" : "+v"(rt[s]));
     auto walk = [&](auto full) {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) {
         if (act && vmt[s] >= thr) {
 #pragma unroll
           for (int w = 0; w < W; ++w) {
-            if ((decltype(full)::value || tpos<DT>(s, w) < lim) && et.x[s][w] >= thr) {
+            const float e = REUNPACK ? unpack<DT>(rt[s], w) : et.x[s][w];
+            if ((decltype(full)::value || tpos<DT>(s, w) < lim) && e >= thr) {
               const int slot = atomicAdd(&sm.bc[0], 1);
-              if (slot < STAGE) sm.keys[slot] = cand_key(et.x[s][w], c * TILE + tpos<DT>(s, w));
+              if (slot < STAGE) sm.keys[slot] = raw_cand(e, tpos<DT>(s, w));
             }
           }
         }
@@ -1103,6 +1120,13 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
     // stage the overflow flag asks for a rescan.
     const int nc = sm.bc[0];
     const bool own32 = nc > SLOTS && nc <= STAGE;
+    // the staged candidates' keys: every one of them to rank the tile's own
+    // 32 largest, else the first SLOTS
+    const int nk = own32 ? nc : (nc < SLOTS ? nc : SLOTS);
+    for (int q = lane; q < nk; q += 64) sm.keys[q] = key_of_raw(sm.keys[q], c * TILE);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (lane < 8) {
       uint64_t word;
       if (lane == 0) word = ((uint64_t)__float_as_uint(m_cd) << 32) | __float_as_uint(m_ct);
