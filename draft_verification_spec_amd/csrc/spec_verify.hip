@@ -23,8 +23,9 @@
 //             tile whose candidate threshold lies above the bound (it may hold
 //             further elements above it) is rescanned, as is a tile whose
 //             candidates overflowed their slots.  The group record (offsets of
-//             the row's log-normaliser, flags, decision) is flagged ready as
-//             soon as the decision is made.
+//             the row's log-normaliser, flags, decision) goes out as soon as
+//             the decision is made; its offsets word is stored complemented,
+//             so a draw that reads it nonzero beside the ready flag has both.
 //             The merge of row k (dispatched after rows 0..k-1) waits for the
 //             sequence's other groups and assembles it: the first rejection j
 //             (greedy: the first draft that differs from the argmax), the
@@ -108,11 +109,12 @@ static_assert(sizeof(TileRec) == 64, "tile record");
 
 // Published per group by its merging workgroup.
 struct GroupRec {
-  float ot, od;            // sampling: offsets m * log2(e)/T + log2(s) of the target / draft row
+  float ot, od;            // sampling: offsets m * log2(e)/T + log2(s) of the target / draft row,
+                           // stored as the complement of their bits (never 0 once written)
   int32_t flags;           // SV_STATUS_* bits of this group's rows and token
   int32_t argmax;          // greedy: top-1 index of the target row
   int32_t accept;          // 1 when the drafted token passed (pair groups)
-  int32_t ready;           // sampling: set to 1 once the fields above are visible
+  int32_t ready;           // sampling: 1, written with the rest (the offsets word validates itself)
 };
 static_assert(sizeof(GroupRec) == 24, "group record");
 
@@ -499,7 +501,9 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         GroupRec gr;
         gr.ot = (float)((double)M_t * P.scd + log2_split(S_t));
         gr.od = pair ? (float)((double)M_d * P.scd + log2_split(S_d)) : 0.f;
-        gr.flags = fl; gr.argmax = -1; gr.accept = acc; gr.ready = 0;
+        gr.ot = __uint_as_float(~__float_as_uint(gr.ot == gr.ot ? gr.ot : __builtin_nanf("")));
+        gr.od = __uint_as_float(~__float_as_uint(gr.od == gr.od ? gr.od : __builtin_nanf("")));
+        gr.flags = fl; gr.argmax = -1; gr.accept = acc; gr.ready = 1;
         st_rec(P.grec + g, gr);
         if (P.lse_t) P.lse_t[(int64_t)b * K1 + i] = (float)((double)M_t / (double)P.T + lg);
       }
@@ -508,13 +512,13 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         if (dst) dst[(int64_t)b * k + i] = (float)pv;
         if (lane == 1 && P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)M_d / (double)P.T + lg);
       }
-      // the group record is out: flag it for the draw and announce it to the
-      // sequence now (the top-32 is not part of it)
+      // the group record is out, ready flag included: a draw takes the
+      // decision once both its (accept, ready) word and its offsets word
+      // (never 0 once written) read nonzero.  The sequence's assembly reads the
+      // whole record once it is complete: announce it after the stores (the
+      // top-32 is not part of it)
       stores_done();
-      if (lane == 0) {
-        st_dev(&P.grec[g].ready, 1);
-        if (i != k) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
-      }
+      if (lane == 0 && i != k) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
     }
 
     if (lane == 0) {
@@ -833,15 +837,20 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
   SeqRec *rec = (SeqRec *)((char *)P.srec + (int64_t)b * SREC_STRIDE);
   const GroupRec *grs = P.grec + (int64_t)b * K1;
   if (wid == 0) {
+    // the residual's and the bonus's uniforms, read before the drawing row is known
+    const float ures = P.uniforms[(int64_t)b * (k + 2) + k], ubon = P.uniforms[(int64_t)b * (k + 2) + k + 1];
     int j = -1;
+    uint64_t ow = 0;                   // lane i: group i's offsets word
     if (K1 <= 64) {
-      // lane i watches group i's (accept, ready) word
+      // lane i watches group i's (accept, ready) word and its offsets word
       const uint64_t *word = (const uint64_t *)&grs[lane < K1 ? lane : 0].accept;
+      const uint64_t *oword = (const uint64_t *)&grs[lane < K1 ? lane : 0].ot;
       uint64_t w = lane < K1 ? ld_dev(word) : 0ull;
+      ow = lane < K1 ? ld_dev(oword) : 0ull;
       const uint64_t all = K1 == 64 ? ~0ull : (1ull << K1) - 1;
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       while (true) {
-        const uint64_t rdy = __ballot(lane < K1 && (w >> 32) != 0) & all;
+        const uint64_t rdy = __ballot(lane < K1 && (w >> 32) != 0 && ow != 0) & all;
         const uint64_t rej = __ballot(lane < k && (w >> 32) != 0 && (uint32_t)w == 0u);
         const uint64_t nr = all & ~rdy;
         const int fz = nr ? __builtin_ctzll(nr) : K1;              // first group not yet in
@@ -854,19 +863,22 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
         }
         __builtin_amdgcn_s_sleep(8);
         if (lane < K1 && (w >> 32) == 0) w = ld_dev(word);
+        if (lane < K1 && ow == 0) ow = ld_dev(oword);
       }
+      if (j >= 0) ow = ((uint64_t)readlane((uint32_t)(ow >> 32), j) << 32) | readlane((uint32_t)ow, j);
     } else if (lane == 0) {
       const int v = wait_at_least(&rec->state, 1, P.fault);
       if (v == 1 || v == 2) j = ld_dev(&rec->j);
       if (j < 0 || j > k) { if (v > 0) atomicOr(P.fault, 2); j = -1; }
       j = v == 1 ? j : -1;
+      if (j >= 0) ow = ld_dev((const uint64_t *)&grs[j].ot);
     }
     if (lane == 0) {
       sm.bc[3] = j;
       if (j >= 0) {
-        sm.f[2][0] = ld_dev(&grs[j].ot);
-        sm.f[2][1] = ld_dev(&grs[j].od);
-        sm.dbc[2] = (double)P.uniforms[(int64_t)b * (k + 2) + (j < k ? k : k + 1)];
+        sm.f[2][0] = __uint_as_float(~(uint32_t)ow);
+        sm.f[2][1] = __uint_as_float(~(uint32_t)(ow >> 32));
+        sm.dbc[2] = (double)(j < k ? ures : ubon);
       }
     }
   }
