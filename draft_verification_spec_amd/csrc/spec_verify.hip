@@ -477,26 +477,26 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     fl = GREEDY ? (fa & SV_STATUS_NAN) : (fa | (pair ? fd : 0));
 
     if (!GREEDY) {
-      // acceptance: lane 0 evaluates p_i(x_i), lane 1 q_i(x_i), side by side
+      // acceptance: lane 0 evaluates e_p = 2^((t_x - m_t) sc), lane 1 e_q for
+      // the draft, side by side; p = e_p / s_t and q = e_q / s_d, and u < min(1,
+      // p / q) is tested as u < 1 and u e_q s_t < e_p s_d (q = 0: p > 0), with
+      // no division on the way to the group record
       int acc = 1;
-      double pv = __builtin_nan("");
+      double ev = __builtin_nan("");
       if (pair) {
         if (x < 0 || x >= V) {
           fl |= SV_STATUS_BAD_TOKEN;
           acc = 0;
         } else if (!fl) {
           const double mm = lane == 0 ? (double)M_t : (double)M_d;
-          const double ss = lane == 0 ? S_t : S_d;
-          pv = exp2_split(((double)lv - mm) * P.scd) / ss;
-          const double p = readlane_d(pv, 0), q = readlane_d(pv, 1);
-          const double ratio = q > 0.0 ? p / q : (p > 0.0 ? __builtin_inf() : 0.0);
-          const double a = ratio < 1.0 ? ratio : 1.0;
-          acc = ((double)__uint_as_float(readlane(__float_as_uint(ui), 0)) < a) ? 1 : 0;
+          ev = exp2_split(((double)lv - mm) * P.scd);
+          const double ep = readlane_d(ev, 0), eq = readlane_d(ev, 1);
+          const double u = (double)__uint_as_float(readlane(__float_as_uint(ui), 0));
+          acc = (u < 1.0 && (eq > 0.0 ? u * eq * S_t < ep * S_d : ep > 0.0)) ? 1 : 0;
         } else {
           acc = 0;
         }
       }
-      const double lg = log_split(lane == 0 ? S_t : S_d);
       if (lane == 0) {
         GroupRec gr;
         gr.ot = (float)((double)M_t * P.scd + log2_split(S_t));
@@ -505,11 +505,13 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         gr.od = __uint_as_float(~__float_as_uint(gr.od == gr.od ? gr.od : __builtin_nanf("")));
         gr.flags = fl; gr.argmax = -1; gr.accept = acc; gr.ready = 1;
         st_rec(P.grec + g, gr);
-        if (P.lse_t) P.lse_t[(int64_t)b * K1 + i] = (float)((double)M_t / (double)P.T + lg);
       }
+      // the aux outputs, after the record
+      const double lg = log_split(lane == 0 ? S_t : S_d);
+      if (lane == 0 && P.lse_t) P.lse_t[(int64_t)b * K1 + i] = (float)((double)M_t / (double)P.T + lg);
       if (pair && lane < 2) {
         float *dst = lane == 0 ? P.p_tok : P.q_tok;
-        if (dst) dst[(int64_t)b * k + i] = (float)pv;
+        if (dst) dst[(int64_t)b * k + i] = (float)(ev / (lane == 0 ? S_t : S_d));
         if (lane == 1 && P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)M_d / (double)P.T + lg);
       }
       // the group record is out, ready flag included: a draw takes the
