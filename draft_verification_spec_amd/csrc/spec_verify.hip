@@ -89,12 +89,12 @@ template <int DT> constexpr bool kStreamNT = DT == SV_F32;
 // Waves per SIMD the kernel is built for: 8 for fp32 (64 VGPRs; at B = 32,
 // k = 15 greedy 83.6 -> 80.3 us, sampling 135.6 -> 132.6 us against 6).  bf16
 // has two builds, chosen per shape by the measured table: the format's budget
-// (6 waves, 80 VGPRs) and a high-occupancy one (7 waves in sampling, 8 in
-// greedy), which keeps more workgroups resident at large batches but measured
-// slower at small ones.  No build uses scratch memory; the SGPRs the compiler
-// spills (kernel arguments, mostly) go to VGPR lanes.
+// (6 waves, 80 VGPRs) and a high-occupancy one (8 waves, 64 VGPRs), which
+// keeps more workgroups resident at large batches but measured slower at small
+// ones.  No build uses scratch memory; the SGPRs the compiler spills (kernel
+// arguments, mostly) go to VGPR lanes.
 template <int DT, bool GREEDY, bool HI> constexpr int kWaves =
-    DT == SV_F32 ? 8 : (HI ? (GREEDY ? 8 : 7) : Fmt<DT>::WAVES);
+    DT == SV_F32 ? 8 : (HI ? 8 : Fmt<DT>::WAVES);
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
 // Published per (group, tile) by the stream workgroups; 8 words.
 struct TileRec {

@@ -1,5 +1,5 @@
 """Measure the verification kernel's two item layouts and, for bf16 logits, its
-two builds (6 waves per SIMD, or 7 in sampling and 8 in greedy) over batch
+two builds (6 or 8 waves per SIMD) over batch
 sizes and draft lengths on the GPU, and write the table the library's
 SV_LAYOUT_AUTO and SV_VARIANT_AUTO use (csrc/sv_dispatch.h) with a summary
 (profiles/dispatch_layout_V151936.md).

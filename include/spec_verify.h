@@ -95,9 +95,8 @@ typedef struct {
                             contiguous run of items per XCD); results are identical */
     int32_t variant;     /* build of the kernel: SV_VARIANT_AUTO (0, the library's measured
                             table), SV_VARIANT_BASE (bf16 at 6 waves per SIMD) or
-                            SV_VARIANT_HIGH_OCC (bf16 sampling at 7 waves per SIMD, bf16
-                            greedy at 8; fp32 has one build, taken for both); results are
-                            identical */
+                            SV_VARIANT_HIGH_OCC (bf16 at 8 waves per SIMD; fp32 has one
+                            build, taken for both); results are identical */
 } sv_aux_t;
 
 #define SV_LAYOUT_AUTO 0
