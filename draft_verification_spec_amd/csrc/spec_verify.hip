@@ -49,7 +49,10 @@
 // as SV_STATUS_SYNC_TIMEOUT) and the kernel still finishes.  Data moves
 // between workgroups through the workspace with device-scope write-through
 // stores and device-scope loads, ordered by waiting for the stores to complete
-// before the counter or flag that announces them is written.  Wave-level
+// before the counter or flag that announces them is written, or as words that
+// are never 0 once written, which the reader reads again until they are (tile
+// records and candidate slots in the base bf16 sampling build, group-record
+// offsets, tile totals).  Wave-level
 // reductions and scans run on DPP row shifts and broadcasts in a fixed order,
 // so every reduction is deterministic.
 //
@@ -96,11 +99,25 @@ template <int DT> constexpr bool kStreamNT = DT == SV_F32;
 template <int DT, bool GREEDY, bool HI> constexpr int kWaves =
     DT == SV_F32 ? 8 : (HI ? 8 : Fmt<DT>::WAVES);
 constexpr int KEYS_PT = MAX_TILES * SLOTS / TPB;   // candidate slots per merge thread
-// Published per (group, tile) by the stream workgroups; 8 words.
+// How a group's merge learns that its tiles' records and candidate slots are
+// out.  Counted: each tile waits for its stores and bumps the group's
+// counter, and the merge waits for the count, then loads records and slots in
+// one round.  Uncounted: the merge reads the records as they land (their
+// words, stored complemented, are never 0 once written), decides, and only
+// then reads the slots each record says are in use, again until written.
+// Uncounted is the base bf16 sampling build's (steady B = 32, k = 3: 29.0 ->
+// 28.0 us; B = 1..4, k = 8: 0.7-0.9 us less); counted measured faster for fp32
+// (wide: 112.6 against 119.5 us), in greedy mode, whose decision needs the
+// top-32 (wide greedy: 64.1 against 71.6 us), and for the high-occupancy
+// build's large batches (B = 256, k = 3: 124.0 against 124.6 us).
+template <int DT, bool GREEDY, bool HI> constexpr bool Uncounted = DT == SV_BF16 && !GREEDY && !HI;
+// Published per (group, tile) by the stream workgroups; 8 words, stored as
+// their complements by the uncounted build (see Uncounted).
 struct TileRec {
   float m_t, m_d;          // tile max of the target / draft row part
   double s_t, s_d;         // sum exp2((x - m) * sc) over the tile part
-  int32_t flags;           // SV_STATUS_* bits: target row part | draft row part << 8
+  int32_t flags;           // SV_STATUS_* bits: target row part | draft row part << 8 (bits
+                           // 0-15), candidate slots in use (16-23), overflow: rescan the tile (24)
   uint32_t kthr;           // ordered key of the candidate threshold (0: every element)
   uint32_t top[LIST];      // ordered keys of 8 lane maxima of distinct lanes, the two
                            // largest of each wave (0: no lane)
@@ -138,7 +155,6 @@ struct Params {
   GroupRec *grec;
   SeqRec *srec;
   uint64_t *cand;                      // [group][tile][SLOTS] candidate keys, 0 = empty
-  int32_t *ovf;                        // [group][tile] 1: more candidates than SLOTS
   uint64_t *dtot;                      // [sequence][tile][2] drawing-row tile totals (residual, p) as
                                        // tot_word: 0 until published
   int32_t B, k, V, nT;
@@ -168,6 +184,7 @@ struct Smem {
   int32_t bc[8];
   double dbc[8];
   uint64_t rescan;                     // row merge: tiles to rescan
+  int32_t i4[MAX_TILES];               // row merge: each tile's candidate slots in use
 };
 
 // ---------------------------------------------------------------- helpers
@@ -422,7 +439,7 @@ __device__ __forceinline__ double log_split(double s) { return log2_split(s) * 0
 
 // Row combine, acceptance decision and top-32 merge of group g (run by its last
 // tile once the others have published), then the sequence's arrival.
-template <int DT, bool GREEDY>
+template <int DT, bool GREEDY, bool HI>
 __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int32_t x, Smem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int nT = P.nT, k = P.k, K1 = k + 1, V = P.V;
@@ -430,28 +447,54 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   const bool pair = G.pair;
   const int nslot = nT * SLOTS;
 
-  // ---- one round of loads: candidate slots (all threads), tile records and
-  // overflow flags (wave 0, lane t: tile t), the drafted token's logits and uniform
+  // ---- one round of loads: tile records (wave 0, lane t: tile t), the
+  // drafted token's logits and uniform, and, in counted mode, the candidate
+  // slots (all threads).  Record words are stored complemented and are never
+  // 0 once written: in uncounted mode waves 0 and 1 read a word again until
+  // it is (a tile's record goes out after its slots)
+  constexpr bool UNC = Uncounted<DT, GREEDY, HI>;
   uint64_t *slots = P.cand + (int64_t)g * nslot;
   uint64_t key[KEYS_PT];
+  if (!UNC) {
 #pragma unroll
-  for (int q = 0; q < KEYS_PT; ++q) {
-    const int a = tid + q * TPB;
-    key[q] = a < nslot ? ld_dev(slots + a) : 0ull;
+    for (int q = 0; q < KEYS_PT; ++q) {
+      const int a = tid + q * TPB;
+      key[q] = a < nslot ? ld_dev(slots + a) : 0ull;
+    }
   }
   // wave 0 takes words 0-3 of tile record `lane` (statistics), wave 1 words
-  // 3-7 (candidate threshold, lane maxima) and the tile's overflow flag
+  // 3-7 (candidate threshold, slots used, overflow, lane maxima)
   uint64_t *rsrc = (uint64_t *)(P.recs + (int64_t)g * nT) + lane * 8;
   uint64_t rw[8];
-  int32_t ov = 0;
   const bool own = wid == 0 && lane < nT, own1 = wid == 1 && lane < nT;
+  auto mine = [&](int q) { return (own && q <= 3) || (own1 && q >= 3); };
 #pragma unroll
-  for (int q = 0; q < 8; ++q) rw[q] = ((own && q <= 3) || (own1 && q >= 3)) ? ld_dev(rsrc + q) : 0ull;
-  if (own1) ov = ld_dev(P.ovf + (int64_t)g * nT + lane);
+  for (int q = 0; q < 8; ++q) rw[q] = mine(q) ? ld_dev(rsrc + q) : ~0ull;
   float lv = 0.f;                              // lane 0: t_x, lane 1: d_x
   float ui = 0.f;
   if (pair && wid == 0 && lane < 2 && x >= 0 && x < V) lv = load_elem<DT>(lane == 0 ? G.trow : G.drow, x);
   if (pair && tid == 0) ui = P.uniforms[(int64_t)b * (k + 2) + i];
+  if (UNC && wid < 2) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      bool miss = false;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) miss |= rw[q] == 0ull;
+      if (!__ballot(miss)) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+        if (lane == 0) atomicOr(P.fault, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (rw[q] == 0ull) rw[q] = ld_dev(rsrc + q);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) rw[q] = mine(q) ? (UNC ? ~rw[q] : rw[q]) : 0ull;
+  // wave 1: each tile's slots in use, for the uncounted slot reads after the decision
+  if (UNC && own1) sm.i4[lane] = (int)((uint32_t)rw[3] >> 16 & 0xffu);
 
   // ---- wave 0: row statistics, decision and group record; wave 1: the row bound
   float M_t = NEG_INF;
@@ -547,7 +590,8 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     }
     // tiles to rescan: candidates overflowed, or the candidate threshold lies
     // above the bound (elements between the two were not published)
-    const uint64_t rs = __ballot(own1 && (ov != 0 || kthr > (rb | Fmt<DT>::LOW)));
+    const bool ov = ((uint32_t)rw[3] >> 24 & 1u) != 0;
+    const uint64_t rs = __ballot(own1 && (ov || kthr > (rb | Fmt<DT>::LOW)));
     if (lane == 0) {
       sm.rescan = rs;
       sm.bc[0] = 0;
@@ -570,17 +614,53 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     seq_finish<DT, GREEDY>(P, b, sm);
   }
 
-  // which slots hold a key (to clear them at the end), so that the keys
-  // themselves are dead across the rescans below
+
+  // uncounted: the candidate slots in use (each tile's count came with its
+  // record); a slot that reads 0 is read again until written (the thread
+  // index passes through an empty asm: recomputing the slot indices costs
+  // less than keeping them live).  Counted: the slots that hold a key (to
+  // clear them at the end), so that the keys themselves are dead across the
+  // rescans below
   uint32_t kheld = 0;
+  int tid2 = tid;
+  if (UNC) asm volatile("" : "+v"(tid2));
+  if (UNC) {
 #pragma unroll
-  for (int q = 0; q < KEYS_PT; ++q) kheld |= key[q] ? 1u << q : 0u;
+    for (int q = 0; q < KEYS_PT; ++q) {
+      const int a = tid2 + q * TPB;
+      const bool want = a < nslot && (a & (SLOTS - 1)) < sm.i4[a / SLOTS];
+      kheld |= want ? 1u << q : 0u;
+      key[q] = want ? ld_dev(slots + a) : 0ull;
+    }
+    if (kheld) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        bool miss = false;
+#pragma unroll
+        for (int q = 0; q < KEYS_PT; ++q) miss |= ((kheld >> q) & 1u) && key[q] == 0ull;
+        if (!miss) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+          atomicOr(P.fault, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int q = 0; q < KEYS_PT; ++q)
+          if (((kheld >> q) & 1u) && key[q] == 0ull) key[q] = ld_dev(slots + tid2 + q * TPB);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < KEYS_PT; ++q) kheld |= key[q] ? 1u << q : 0u;
+  }
 
   // ---- candidates at or above the bound: slots of complete tiles, then rescans
   if (!nanrow) {
+    int tid3 = tid;
+    if (UNC) asm volatile("" : "+v"(tid3));
 #pragma unroll
     for (int q = 0; q < KEYS_PT; ++q) {
-      const int a = tid + q * TPB;
+      const int a = tid3 + q * TPB;
       if (a < nslot && key[q] && !((rs >> (a / SLOTS)) & 1u) && (uint32_t)(key[q] >> 32) >= rb) {
         const int pos = atomicAdd(&sm.bc[0], 1);
         if (pos < MERGE_CAP) sm.keys[pos] = key[q];
@@ -648,9 +728,11 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     stores_done();
     if (i != k && tid == 0) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
   }
+  int tid4 = tid;
+  if (UNC) asm volatile("" : "+v"(tid4));
 #pragma unroll
   for (int q = 0; q < KEYS_PT; ++q) {
-    const int a = tid + q * TPB;
+    const int a = tid4 + q * TPB;
     if ((kheld >> q) & 1u) st_dev(slots + a, (uint64_t)0);
   }
   if (own) {
@@ -661,7 +743,6 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     for (int q = 0; q < 8; ++q)
       if (q >= q0) st_dev(rsrc + q, (uint64_t)0);
   }
-  if (ov) st_dev(P.ovf + (int64_t)g * nT + lane, 0);
   if (!GREEDY || i != k) return;
   // row k is the sequence's last group: wait for the others, then assemble
   if (tid == 0) {
@@ -897,7 +978,8 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
     if (wid == 0) {
       const uint64_t *rk = (const uint64_t *)(P.recs + (int64_t)(b * K1 + k) * nT) + lane * 8;
       const bool own = lane < nT;
-      const uint64_t w0 = own ? ld_dev(rk) : 0ull, w1 = own ? ld_dev(rk + 1) : 0ull;
+      constexpr uint64_t cpl = Uncounted<DT, false, HI> ? ~0ull : 0ull;   // complemented records
+      const uint64_t w0 = own ? ld_dev(rk) ^ cpl : 0ull, w1 = own ? ld_dev(rk + 1) ^ cpl : 0ull;
       const float mt = __uint_as_float((uint32_t)w0);
       const double tm = own && mt != NEG_INF
                             ? __builtin_bit_cast(double, w1) * exp2_split((double)mt * (double)P.sc - (double)ot)
@@ -1141,18 +1223,14 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < 8) {
-      uint64_t word;
-      if (lane == 0) word = ((uint64_t)__float_as_uint(m_cd) << 32) | __float_as_uint(m_ct);
-      else if (lane == 1) word = __builtin_bit_cast(uint64_t, s_ct);
-      else if (lane == 2) word = __builtin_bit_cast(uint64_t, s_cd);
-      else if (lane == 3) word = ((uint64_t)(own32 ? 0u : kthr) << 32) | (uint32_t)(f_ct | (f_cd << 8));
-      else word = ((uint64_t)sm.w8[2 * (lane - 4) + 1] << 32) | sm.w8[2 * (lane - 4)];
-      st_dev((uint64_t *)(P.recs + item) + lane, word);
-    }
+    // the slots first, then the record, whose words go out complemented (a
+    // NaN maximum or sum and an all-ones key canonical, so no word is 0 once
+    // written): the merge reads a word again until it is nonzero, and takes
+    // the record's count of slots in use, with no store wait and no counter
+    // between the tile and its merge
+    const int npub = own32 ? SLOTS : (nc < SLOTS ? nc : SLOTS);
     if (!own32) {
-      if (lane < SLOTS && lane < nc) st_dev(P.cand + (int64_t)item * SLOTS + lane, sm.keys[lane]);
-      if (lane == 0 && nc > STAGE) st_dev(P.ovf + item, 1);
+      if (lane < npub) st_dev(P.cand + (int64_t)item * SLOTS + lane, sm.keys[lane]);
     } else {
       for (int q = lane; q < nc; q += 64) {
         const uint64_t kq = sm.keys[q];
@@ -1161,20 +1239,37 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
         if (rank < SLOTS) st_dev(P.cand + (int64_t)item * SLOTS + rank, kq);
       }
     }
-    stores_done();
+    if (lane < 8) {
+      auto canon_f = [](float v) { return !Uncounted<DT, GREEDY, HI> || v == v ? __float_as_uint(v) : 0x7fc00000u; };
+      auto canon_k = [](uint32_t v) { return Uncounted<DT, GREEDY, HI> && v == 0xffffffffu ? 0xfffffffeu : v; };
+      uint64_t word;
+      if (lane == 0) word = ((uint64_t)canon_f(m_cd) << 32) | canon_f(m_ct);
+      else if (lane == 1)
+        word = !Uncounted<DT, GREEDY, HI> || s_ct == s_ct ? __builtin_bit_cast(uint64_t, s_ct) : 0x7ff8000000000000ull;
+      else if (lane == 2)
+        word = !Uncounted<DT, GREEDY, HI> || s_cd == s_cd ? __builtin_bit_cast(uint64_t, s_cd) : 0x7ff8000000000000ull;
+      else if (lane == 3)
+        word = ((uint64_t)(own32 ? 0u : kthr) << 32) | (uint32_t)(f_ct | (f_cd << 8)) | ((uint32_t)npub << 16) |
+               (nc > STAGE ? 1u << 24 : 0u);
+      else word = ((uint64_t)canon_k(sm.w8[2 * (lane - 4) + 1]) << 32) | canon_k(sm.w8[2 * (lane - 4)]);
+      st_dev((uint64_t *)(P.recs + item) + lane, Uncounted<DT, GREEDY, HI> ? ~word : word);
+    }
+    if (!Uncounted<DT, GREEDY, HI>) {
+      stores_done();
+      if (c != P.nT - 1 && lane == 0) add_dev_noret(P.garrive + (int64_t)G.g * CTR, 1);
+    }
   }
-  if (c != P.nT - 1) {                                   // not the group's last tile: announce and leave
-    if (tid == 0) add_dev_noret(P.garrive + (int64_t)G.g * CTR, 1);
-    return;
+  if (c != P.nT - 1) return;                             // not the group's last tile: done
+  if (!Uncounted<DT, GREEDY, HI>) {
+    // the group's last tile waits for the others' count before it merges
+    if (tid == 0) {
+      const int v = wait_at_least(P.garrive + (int64_t)G.g * CTR, P.nT - 1, P.fault);
+      if (v > P.nT - 1) atomicOr(P.fault, 2);                        // workspace not zero-filled
+      st_dev(P.garrive + (int64_t)G.g * CTR, 0);
+    }
+    __syncthreads();
   }
-  // the group's last tile: wait for the other tiles, then merge
-  if (tid == 0) {
-    const int v = wait_at_least(P.garrive + (int64_t)G.g * CTR, P.nT - 1, P.fault);
-    if (v > P.nT - 1) atomicOr(P.fault, 2);                          // workspace not zero-filled
-    st_dev(P.garrive + (int64_t)G.g * CTR, 0);
-  }
-  __syncthreads();
-  group_finish<DT, GREEDY>(P, G, xtok, sm);
+  group_finish<DT, GREEDY, HI>(P, G, xtok, sm);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1333,7 +1428,6 @@ int verify_impl(const sv_shape_t *shape, const void *target_logits, const void *
   P.grec = (GroupRec *)(ws + L.grec);
   P.srec = (SeqRec *)(ws + L.srec);
   P.cand = (uint64_t *)(ws + L.cand);
-  P.ovf = (int32_t *)(ws + L.ovf);
   P.dtot = (uint64_t *)(ws + L.dtot);
   P.B = s.B;
   P.k = s.k;

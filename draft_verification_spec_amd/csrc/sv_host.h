@@ -30,7 +30,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace sections, each 256-byte aligned, in this order; the fault word sits
 // at offset 0 for every shape.
 struct Layout {
-  size_t fault, garrive, sarrive, ddone, recs, grec, srec, cand, ovf, dtot, total;
+  size_t fault, garrive, sarrive, ddone, recs, grec, srec, cand, dtot, total;
 };
 
 inline Layout layout_for(int B, int k, int V, int dtype) {
@@ -46,7 +46,6 @@ inline Layout layout_for(int B, int k, int V, int dtype) {
   L.grec = o;    o = align256(o + groups * GROUP_REC_BYTES);
   L.srec = o;    o = align256(o + (size_t)B * SEQ_REC_BYTES);
   L.cand = o;    o = align256(o + groups * nT * SLOTS * sizeof(uint64_t));
-  L.ovf = o;     o = align256(o + groups * nT * sizeof(int32_t));
   L.dtot = o;    o = align256(o + (size_t)B * nT * 2 * sizeof(double));
   L.total = o;
   return L;
