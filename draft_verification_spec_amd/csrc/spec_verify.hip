@@ -82,6 +82,7 @@ constexpr int LIST = 8;                // lane maxima a tile record keeps
 constexpr int SLOTS = 32;              // candidate slots per tile
 constexpr int MERGE_CAP = 512;         // candidates a row merge ranks in LDS
 constexpr int STAGE = 128;             // candidates a tile stages in LDS (its top SLOTS are published)
+constexpr int STAGE_V = 128;           // vectors holding candidates a tile stages in LDS
 constexpr int TOPK = SV_TOPK;
 constexpr int MAX_TILES = 64;          // tiles per row: one merge lane each
 // The streaming loads are marked nontemporal for fp32 logits only: with bf16
@@ -167,7 +168,7 @@ struct Params {
 
 struct Smem {
   union {
-    uint64_t keys[MERGE_CAP];          // stream: the tile's candidates; row merge: those at or above the bound
+    uint64_t keys[MERGE_CAP];          // row merge: the candidates at or above the bound
     struct {                           // exact top-32 fallback
       uint32_t hist[2048];
       int32_t part[TPB];
@@ -176,6 +177,11 @@ struct Smem {
     struct {                           // draw: the crossing thread's elements
       uint32_t t[NSEG * 4], d[NSEG * 4];
     } walk;
+    struct {                           // stream: vectors that hold candidates, then the candidates
+      u32x4 v[STAGE_V];                // raw vector
+      int32_t pos[STAGE_V];            // tile position of its first element
+      uint64_t ck[STAGE];              // candidates: value bits and tile position, then keys
+    } st;
   };
   uint32_t w8[LIST];                   // stream: each wave's two largest lane maxima
   float f[4][NWAVE];
@@ -1064,7 +1070,10 @@ __device__ __forceinline__ void draw_tile(const Params &P, int b, int c, Smem &s
       if (!sm.bc[4]) break;
       rmode = false;                   // no residual mass left: draw from p_j
     }
-    if (sm.bc[2] == c) draw_crossing<DT>(P, b, c, j, rt, rd, rmode, ot, od, mine, base, rec, sm);
+    // (fp32: j read again from LDS, not held in registers across the rounds,
+    // which keeps this build within 64 registers without spilling)
+    const int jc = DT == SV_F32 ? *(volatile int32_t *)&sm.bc[3] : j;
+    if (sm.bc[2] == c) draw_crossing<DT>(P, b, c, jc, rt, rd, rmode, ot, od, mine, base, rec, sm);
   }
   // every draw workgroup of the sequence reports; the last clears its state
   const int old = count_done(P.ddone + (int64_t)b * CTR, &sm.bc[7]);
@@ -1156,39 +1165,25 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
   for (int q = 0; q < LIST; ++q) { const uint32_t v = sm.w8[q]; if (v && v < kthr) kthr = v; }
   if (kthr == 0xffffffffu) kthr = 0u;
 
-  // candidates: elements at or above the threshold, gathered in LDS position
-  // by position (a position that holds none in any lane costs one compare;
-  // the slot reservation is one LDS atomic per wave and position) as raw
-  // value bits and tile position; wave 0 forms the ordered keys of those it
-  // publishes
+  // candidates: elements at or above the threshold.  Every vector whose
+  // maximum reaches it is staged raw in LDS with its tile position (one LDS
+  // slot reservation per wave and vector, no per-element work); wave 0 takes
+  // the candidates out of the staged vectors and forms the ordered keys of
+  // those it publishes
+  const float thr = key_value(kthr);
+  const int lim = V - c * TILE;                          // tile positions < lim exist
   {
-    const float thr = key_value(kthr);
-    const int lim = V - c * TILE;                        // tile positions < lim exist
     const bool act = has_elem && tkey >= kthr;           // lanes that may hold candidates
-    // (the greedy high-occupancy build, at 64 registers, unpacks the walked
-    // vectors again: its packed elements pass through an empty asm so that
-    // the unpacked copy is not kept live from the statistics)
-    constexpr bool REUNPACK = GREEDY && HI;
-    if (REUNPACK)
 #pragma unroll
-      for (int s = 0; s < NSEG; ++s) asm volatile("" : "+v"(rt[s]));
-    auto walk = [&](auto full) {
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s) {
-        if (act && vmt[s] >= thr) {
-#pragma unroll
-          for (int w = 0; w < W; ++w) {
-            const float e = REUNPACK ? unpack<DT>(rt[s], w) : et.x[s][w];
-            if ((decltype(full)::value || tpos<DT>(s, w) < lim) && e >= thr) {
-              const int slot = atomicAdd(&sm.bc[0], 1);
-              if (slot < STAGE) sm.keys[slot] = raw_cand(e, tpos<DT>(s, w));
-            }
-          }
+    for (int s = 0; s < NSEG; ++s) {
+      if (act && vmt[s] >= thr) {
+        const int slot = atomicAdd(&sm.bc[0], 1);
+        if (slot < STAGE_V) {
+          sm.st.v[slot] = rt[s];
+          sm.st.pos[slot] = tpos<DT>(s, 0);
         }
       }
-    };
-    if (lim >= TILE) walk(std::true_type());
-    else walk(std::false_type());
+    }
   }
   // wave 0 publishes the record and the candidates (one store for all of
   // them), so the other waves of a tile that does not merge are done here
@@ -1214,12 +1209,39 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
     // other elements each lie below 32 published ones, so none can be among
     // the row's 32 largest and the merge never rescans the tile.  Beyond the
     // stage the overflow flag asks for a rescan.
-    const int nc = sm.bc[0];
-    const bool own32 = nc > SLOTS && nc <= STAGE;
+    // the candidates of the staged vectors (lane q: vector q), element by
+    // element, packed by ballot as value bits and tile position
+    const int nv = sm.bc[0];
+    const int nvs = nv < STAGE_V ? nv : STAGE_V;
+    int nc = 0;
+    for (int q0 = 0; q0 < nvs; q0 += 64) {
+      const int q = q0 + lane;
+      const bool have = q < nvs;
+      const u32x4 v = have ? sm.st.v[q] : u32x4{0u, 0u, 0u, 0u};
+      const int p0 = have ? sm.st.pos[q] : 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float e = unpack<DT>(v, w);
+        const bool hit = have && p0 + w < lim && e >= thr;
+        const uint64_t m = __ballot(hit);
+        if (hit) {
+          const int at = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (at < STAGE) sm.st.ck[at] = raw_cand(e, p0 + w);
+        }
+        nc += (int)__builtin_popcountll(m);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // more vectors than the stage holds, or more candidates: the merge rescans
+    const bool ovf = nv > STAGE_V || nc > STAGE;
+    const bool own32 = !ovf && nc > SLOTS;
     // the staged candidates' keys: every one of them to rank the tile's own
     // 32 largest, else the first SLOTS
     const int nk = own32 ? nc : (nc < SLOTS ? nc : SLOTS);
-    for (int q = lane; q < nk; q += 64) sm.keys[q] = key_of_raw(sm.keys[q], c * TILE);
+    for (int q = lane; q < nk; q += 64) sm.st.ck[q] = key_of_raw(sm.st.ck[q], c * TILE);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1230,12 +1252,12 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
     // between the tile and its merge
     const int npub = own32 ? SLOTS : (nc < SLOTS ? nc : SLOTS);
     if (!own32) {
-      if (lane < npub) st_dev(P.cand + (int64_t)item * SLOTS + lane, sm.keys[lane]);
+      if (lane < npub) st_dev(P.cand + (int64_t)item * SLOTS + lane, sm.st.ck[lane]);
     } else {
       for (int q = lane; q < nc; q += 64) {
-        const uint64_t kq = sm.keys[q];
+        const uint64_t kq = sm.st.ck[q];
         int rank = 0;
-        for (int jj = 0; jj < nc; ++jj) rank += sm.keys[jj] > kq;
+        for (int jj = 0; jj < nc; ++jj) rank += sm.st.ck[jj] > kq;
         if (rank < SLOTS) st_dev(P.cand + (int64_t)item * SLOTS + rank, kq);
       }
     }
@@ -1250,7 +1272,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
         word = !Uncounted<DT, GREEDY, HI> || s_cd == s_cd ? __builtin_bit_cast(uint64_t, s_cd) : 0x7ff8000000000000ull;
       else if (lane == 3)
         word = ((uint64_t)(own32 ? 0u : kthr) << 32) | (uint32_t)(f_ct | (f_cd << 8)) | ((uint32_t)npub << 16) |
-               (nc > STAGE ? 1u << 24 : 0u);
+               (ovf ? 1u << 24 : 0u);
       else word = ((uint64_t)canon_k(sm.w8[2 * (lane - 4) + 1]) << 32) | canon_k(sm.w8[2 * (lane - 4)]);
       st_dev((uint64_t *)(P.recs + item) + lane, Uncounted<DT, GREEDY, HI> ? ~word : word);
     }
