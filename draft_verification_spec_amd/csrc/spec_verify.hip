@@ -443,6 +443,37 @@ __device__ __forceinline__ double log2_split(double s) {
 }
 __device__ __forceinline__ double log_split(double s) { return log2_split(s) * 0.6931471805599453; }
 
+// A tile's statistics from its waves' entries in LDS: maxima, flags and, in
+// sampling mode, the exp sums rescaled to the tile maxima in wave order.
+struct TileStats {
+  float m_t, m_d;
+  int f_t, f_d;
+  double s_t, s_d;
+};
+template <bool GREEDY> __device__ __forceinline__ TileStats tile_stats(const Smem &sm, float sc) {
+  TileStats r;
+  r.m_t = sm.f[0][0]; r.m_d = sm.f[1][0];
+  r.f_t = sm.i[0][0]; r.f_d = sm.i[1][0];
+  for (int w = 1; w < NWAVE; ++w) {
+    r.m_t = fmaxf(r.m_t, sm.f[0][w]); r.m_d = fmaxf(r.m_d, sm.f[1][w]);
+    r.f_t |= sm.i[0][w]; r.f_d |= sm.i[1][w];
+  }
+  r.s_t = 0.0; r.s_d = 0.0;
+  if (!GREEDY)
+    for (int w = 0; w < NWAVE; ++w) {
+      r.s_t += rescale(sm.d[0][w], sm.f[0][w], r.m_t, sc);
+      r.s_d += rescale(sm.d[1][w], sm.f[1][w], r.m_d, sc);
+    }
+  return r;
+}
+// Words 0-2 of a tile record (maxima; target sum; draft sum), NaN canonical
+// in the uncounted build so that the complement of a word is never 0.
+template <bool UNC> __device__ __forceinline__ uint64_t stat_word(const TileStats &t, int q) {
+  auto canon_f = [](float v) { return !UNC || v == v ? __float_as_uint(v) : 0x7fc00000u; };
+  auto canon_d = [](double v) { return !UNC || v == v ? __builtin_bit_cast(uint64_t, v) : 0x7ff8000000000000ull; };
+  return q == 0 ? ((uint64_t)canon_f(t.m_d) << 32) | canon_f(t.m_t) : canon_d(q == 1 ? t.s_t : t.s_d);
+}
+
 // Row combine, acceptance decision and top-32 merge of group g (run by its last
 // tile once the others have published), then the sequence's arrival.
 template <int DT, bool GREEDY, bool HI>
@@ -600,7 +631,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     const uint64_t rs = __ballot(own1 && (ov || kthr > (rb | Fmt<DT>::LOW)));
     if (lane == 0) {
       sm.rescan = rs;
-      sm.bc[0] = 0;
+      sm.bc[5] = 0;
       sm.bc[1] = (int)rb;
     }
   }
@@ -608,25 +639,13 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
   const uint32_t rb = (uint32_t)sm.bc[1];
   const bool nanrow = (sm.bc[2] & SV_STATUS_NAN) != 0;
   const uint64_t rs = sm.rescan;
-  if (!GREEDY && i == k) {
-    // sampling: the sequence's assembly needs no top-32, so row k assembles
-    // the sequence (once the other groups have announced) before its own merge
-    if (tid == 0) {
-      const int v = wait_at_least(P.sarrive + (int64_t)b * CTR, k, P.fault);
-      if (v > k) atomicOr(P.fault, 2);                               // workspace not zero-filled
-      st_dev(P.sarrive + (int64_t)b * CTR, 0);
-    }
-    __syncthreads();
-    seq_finish<DT, GREEDY>(P, b, sm);
-  }
-
-
   // uncounted: the candidate slots in use (each tile's count came with its
-  // record); a slot that reads 0 is read again until written (the thread
-  // index passes through an empty asm: recomputing the slot indices costs
-  // less than keeping them live).  Counted: the slots that hold a key (to
-  // clear them at the end), so that the keys themselves are dead across the
-  // rescans below
+  // record), read now, so that in row k's merge they arrive while the
+  // sequence is assembled; a slot that reads 0 is read again until written
+  // (the thread index passes through an empty asm: recomputing the slot
+  // indices costs less than keeping them live).  Counted: the slots that hold
+  // a key (to clear them at the end), so that the keys themselves are dead
+  // across the rescans below
   uint32_t kheld = 0;
   int tid2 = tid;
   if (UNC) asm volatile("" : "+v"(tid2));
@@ -638,6 +657,19 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
       kheld |= want ? 1u << q : 0u;
       key[q] = want ? ld_dev(slots + a) : 0ull;
     }
+  }
+  if (!GREEDY && i == k) {
+    // sampling: the sequence's assembly needs no top-32, so row k assembles
+    // the sequence (once the other groups have announced) before its own merge
+    if (tid == 0) {
+      const int v = wait_at_least(P.sarrive + (int64_t)b * CTR, k, P.fault);
+      if (v > k) atomicOr(P.fault, 2);                               // workspace not zero-filled
+      st_dev(P.sarrive + (int64_t)b * CTR, 0);
+    }
+    __syncthreads();
+    seq_finish<DT, GREEDY>(P, b, sm);
+  }
+  if (UNC) {
     if (kheld) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       while (true) {
@@ -668,7 +700,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     for (int q = 0; q < KEYS_PT; ++q) {
       const int a = tid3 + q * TPB;
       if (a < nslot && key[q] && !((rs >> (a / SLOTS)) & 1u) && (uint32_t)(key[q] >> 32) >= rb) {
-        const int pos = atomicAdd(&sm.bc[0], 1);
+        const int pos = atomicAdd(&sm.bc[5], 1);
         if (pos < MERGE_CAP) sm.keys[pos] = key[q];
       }
     }
@@ -691,7 +723,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
             const float xv = unpack<DT>(r[s], w);
             const int x = x0 + tpos<DT>(s, w);
             if (x < V && xv == xv && ordered_key(xv) >= rb) {
-              const int pos = atomicAdd(&sm.bc[0], 1);
+              const int pos = atomicAdd(&sm.bc[5], 1);
               if (pos < MERGE_CAP) sm.keys[pos] = cand_key(xv, x);
             }
           }
@@ -699,7 +731,7 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
     }
   }
   __syncthreads();
-  const int n = sm.bc[0];
+  const int n = sm.bc[5];
   float *oval = P.topk_val + ((int64_t)b * K1 + i) * TOPK;
   int32_t *oidx = P.topk_idx + ((int64_t)b * K1 + i) * TOPK;
   if (nanrow) {
@@ -769,6 +801,19 @@ template <int DT> __device__ __forceinline__ void unpack_all(const u32x4 (&r)[NS
   for (int s = 0; s < NSEG; ++s)
 #pragma unroll
     for (int w = 0; w < Fmt<DT>::W; ++w) e.x[s][w] = unpack<DT>(r[s], w);
+}
+// Vector s of a thread's elements packed again as loaded (bf16: the high
+// halves of two fp32 values per word; fp32: the bits).
+template <int DT> __device__ __forceinline__ u32x4 repack(const Elems<DT> &e, int s) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (DT == SV_BF16)
+      v[q] = __builtin_amdgcn_perm(__float_as_uint(e.x[s][2 * q + 1]), __float_as_uint(e.x[s][2 * q]), 0x07060302u);
+    else
+      v[q] = __float_as_uint(e.x[s][q]);
+  }
+  return v;
 }
 template <int DT> __device__ __forceinline__ float vmax_of(const Elems<DT> &e, int s) {
   float m = e.x[s][0];
@@ -1174,12 +1219,16 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
   const int lim = V - c * TILE;                          // tile positions < lim exist
   {
     const bool act = has_elem && tkey >= kthr;           // lanes that may hold candidates
+    // (the high-occupancy bf16 sampling build, at 64 registers, packs a
+    // staged vector again from its unpacked elements, so that the packed tile
+    // is not held live across the statistics)
+    constexpr bool REPACK = DT == SV_BF16 && HI && !GREEDY;
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
       if (act && vmt[s] >= thr) {
         const int slot = atomicAdd(&sm.bc[0], 1);
         if (slot < STAGE_V) {
-          sm.st.v[slot] = rt[s];
+          sm.st.v[slot] = REPACK ? repack<DT>(et, s) : rt[s];
           sm.st.pos[slot] = tpos<DT>(s, 0);
         }
       }
@@ -1187,28 +1236,14 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
   }
   // wave 0 publishes the record and the candidates (one store for all of
   // them), so the other waves of a tile that does not merge are done here
+  constexpr bool UNC = Uncounted<DT, GREEDY, HI>;
+  const bool last = c == P.nT - 1;
   __syncthreads();
-  if (wid != 0 && c != P.nT - 1) return;
+  if (wid != 0 && !last) return;
 
   // the tile record (wave 0: lanes 0-7 write one word each)
   if (wid == 0) {
-    float m_ct = sm.f[0][0], m_cd = sm.f[1][0];
-    int f_ct = sm.i[0][0], f_cd = sm.i[1][0];
-    for (int w = 1; w < NWAVE; ++w) {
-      m_ct = fmaxf(m_ct, sm.f[0][w]); m_cd = fmaxf(m_cd, sm.f[1][w]);
-      f_ct |= sm.i[0][w]; f_cd |= sm.i[1][w];
-    }
-    double s_ct = 0.0, s_cd = 0.0;
-    if (!GREEDY)
-      for (int w = 0; w < NWAVE; ++w) {
-        s_ct += rescale(sm.d[0][w], sm.f[0][w], m_ct, P.sc);
-        s_cd += rescale(sm.d[1][w], sm.f[1][w], m_cd, P.sc);
-      }
-    // more candidates than slots, all of them staged: the tile publishes its
-    // own 32 largest (by key, ranked by counting) and a threshold of 0.  Its
-    // other elements each lie below 32 published ones, so none can be among
-    // the row's 32 largest and the merge never rescans the tile.  Beyond the
-    // stage the overflow flag asks for a rescan.
+    const TileStats ts = tile_stats<GREEDY>(sm, P.sc);
     // the candidates of the staged vectors (lane q: vector q), element by
     // element, packed by ballot as value bits and tile position
     const int nv = sm.bc[0];
@@ -1235,7 +1270,12 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // more vectors than the stage holds, or more candidates: the merge rescans
+    // more vectors than the stage holds, or more candidates: the merge
+    // rescans.  More candidates than slots, all of them staged: the tile
+    // publishes its own 32 largest (by key, ranked by counting) and a
+    // threshold of 0.  Its other elements each lie below 32 published ones,
+    // so none can be among the row's 32 largest and the merge never rescans
+    // the tile
     const bool ovf = nv > STAGE_V || nc > STAGE;
     const bool own32 = !ovf && nc > SLOTS;
     // the staged candidates' keys: every one of them to rank the tile's own
@@ -1262,27 +1302,23 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(kWaves<DT, 
       }
     }
     if (lane < 8) {
-      auto canon_f = [](float v) { return !Uncounted<DT, GREEDY, HI> || v == v ? __float_as_uint(v) : 0x7fc00000u; };
-      auto canon_k = [](uint32_t v) { return Uncounted<DT, GREEDY, HI> && v == 0xffffffffu ? 0xfffffffeu : v; };
+      auto canon_k = [](uint32_t v) { return UNC && v == 0xffffffffu ? 0xfffffffeu : v; };
       uint64_t word;
-      if (lane == 0) word = ((uint64_t)canon_f(m_cd) << 32) | canon_f(m_ct);
-      else if (lane == 1)
-        word = !Uncounted<DT, GREEDY, HI> || s_ct == s_ct ? __builtin_bit_cast(uint64_t, s_ct) : 0x7ff8000000000000ull;
-      else if (lane == 2)
-        word = !Uncounted<DT, GREEDY, HI> || s_cd == s_cd ? __builtin_bit_cast(uint64_t, s_cd) : 0x7ff8000000000000ull;
+      if (lane < 3) word = stat_word<UNC>(ts, lane);
       else if (lane == 3)
-        word = ((uint64_t)(own32 ? 0u : kthr) << 32) | (uint32_t)(f_ct | (f_cd << 8)) | ((uint32_t)npub << 16) |
+        word = ((uint64_t)(own32 ? 0u : kthr) << 32) | (uint32_t)(ts.f_t | (ts.f_d << 8)) | ((uint32_t)npub << 16) |
                (ovf ? 1u << 24 : 0u);
       else word = ((uint64_t)canon_k(sm.w8[2 * (lane - 4) + 1]) << 32) | canon_k(sm.w8[2 * (lane - 4)]);
-      st_dev((uint64_t *)(P.recs + item) + lane, Uncounted<DT, GREEDY, HI> ? ~word : word);
+      st_dev((uint64_t *)(P.recs + item) + lane, UNC ? ~word : word);
     }
-    if (!Uncounted<DT, GREEDY, HI>) {
+    // counted: the stores complete before the count
+    if (!UNC) {
       stores_done();
-      if (c != P.nT - 1 && lane == 0) add_dev_noret(P.garrive + (int64_t)G.g * CTR, 1);
+      if (!last && lane == 0) add_dev_noret(P.garrive + (int64_t)G.g * CTR, 1);
     }
   }
-  if (c != P.nT - 1) return;                             // not the group's last tile: done
-  if (!Uncounted<DT, GREEDY, HI>) {
+  if (!last) return;                                     // not the group's last tile: done
+  if (!UNC) {
     // the group's last tile waits for the others' count before it merges
     if (tid == 0) {
       const int v = wait_at_least(P.garrive + (int64_t)G.g * CTR, P.nT - 1, P.fault);
