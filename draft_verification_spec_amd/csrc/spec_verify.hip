@@ -364,6 +364,29 @@ template <int DT, bool GREEDY> __device__ __forceinline__ Geo geo(const Params &
   return G;
 }
 
+// A sampling group record, read word by word until each is nonzero (each is
+// never 0 once written); bounded, as every wait.
+__device__ __forceinline__ GroupRec poll_rec(const GroupRec *src, int32_t *fault) {
+  const uint64_t *s = (const uint64_t *)src;
+  uint64_t w[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) w[q] = ld_dev(s + q);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (!w[0] || !w[1] || !w[2]) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+      atomicOr(fault, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (!w[q]) w[q] = ld_dev(s + q);
+  }
+  GroupRec r;
+  __builtin_memcpy(&r, w, sizeof(r));
+  return r;
+}
+
 // Sequence assembly (run by the merge of row k once the sequence's other
 // groups have published): status, first rejection j, and the tokens; greedy
 // emits everything, sampling leaves the drawn token to the draw workgroups.
@@ -379,7 +402,7 @@ __device__ __forceinline__ void seq_finish(const Params &P, int b, Smem &sm) {
   for (int i0 = 0; i0 < k + 2; i0 += TPB) {
     const int i = i0 + tid;
     GroupRec r = {};
-    if (i < K1) r = ld_rec(P.grec + (int64_t)b * K1 + i);
+    if (i < K1) r = GREEDY ? ld_rec(P.grec + (int64_t)b * K1 + i) : poll_rec(P.grec + (int64_t)b * K1 + i, P.fault);
     const int32_t x = i < k ? P.tokens[(int64_t)b * k + i] : 0;
     const float u = (!GREEDY && i < k + 2) ? P.uniforms[(int64_t)b * (k + 2) + i] : 0.5f;
     if (i < K1) {
@@ -594,13 +617,11 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
         if (dst) dst[(int64_t)b * k + i] = (float)(ev / (lane == 0 ? S_t : S_d));
         if (lane == 1 && P.lse_d) P.lse_d[(int64_t)b * k + i] = (float)((double)M_d / (double)P.T + lg);
       }
-      // the group record is out, ready flag included: a draw takes the
-      // decision once both its (accept, ready) word and its offsets word
-      // (never 0 once written) read nonzero.  The sequence's assembly reads the
-      // whole record once it is complete: announce it after the stores (the
-      // top-32 is not part of it)
-      stores_done();
-      if (lane == 0 && i != k) add_dev_noret(P.sarrive + (int64_t)b * CTR, 1);
+      // the group record is out, ready flag included, with no wait for its
+      // stores: each of its three words is never 0 once written (the offsets
+      // complemented, argmax -1 beside the flags, ready beside accept), so the
+      // draws and the sequence's assembly read a word again until it is
+      // nonzero.  (The top-32 is not part of it.)
     }
 
     if (lane == 0) {
@@ -658,17 +679,9 @@ __device__ __forceinline__ void group_finish(const Params &P, const Geo &G, int3
       key[q] = want ? ld_dev(slots + a) : 0ull;
     }
   }
-  if (!GREEDY && i == k) {
-    // sampling: the sequence's assembly needs no top-32, so row k assembles
-    // the sequence (once the other groups have announced) before its own merge
-    if (tid == 0) {
-      const int v = wait_at_least(P.sarrive + (int64_t)b * CTR, k, P.fault);
-      if (v > k) atomicOr(P.fault, 2);                               // workspace not zero-filled
-      st_dev(P.sarrive + (int64_t)b * CTR, 0);
-    }
-    __syncthreads();
-    seq_finish<DT, GREEDY>(P, b, sm);
-  }
+  // sampling: the sequence's assembly needs no top-32, so row k assembles
+  // the sequence (reading the group records as they land) before its own merge
+  if (!GREEDY && i == k) seq_finish<DT, GREEDY>(P, b, sm);
   if (UNC) {
     if (kheld) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
