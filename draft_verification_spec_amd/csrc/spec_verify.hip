@@ -24,8 +24,9 @@
 //             further elements above it) is rescanned, as is a tile whose
 //             candidates overflowed their slots.  The group record (offsets of
 //             the row's log-normaliser, flags, decision) goes out as soon as
-//             the decision is made; its offsets word is stored complemented,
-//             so a draw that reads it nonzero beside the ready flag has both.
+//             the decision is made; each of its words is never 0 once written
+//             (the offsets word stored complemented), so a draw or the
+//             assembly that reads them nonzero has the record.
 //             The merge of row k (dispatched after rows 0..k-1) waits for the
 //             sequence's other groups and assembles it: the first rejection j
 //             (greedy: the first draft that differs from the argmax), the
@@ -51,8 +52,8 @@
 // stores and device-scope loads, ordered by waiting for the stores to complete
 // before the counter or flag that announces them is written, or as words that
 // are never 0 once written, which the reader reads again until they are (tile
-// records and candidate slots in the base bf16 sampling build, group-record
-// offsets, tile totals).  Wave-level
+// records and candidate slots in the base bf16 sampling build, group records
+// in sampling mode, tile totals).  Wave-level
 // reductions and scans run on DPP row shifts and broadcasts in a fixed order,
 // so every reduction is deterministic.
 //
